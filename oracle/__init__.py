@@ -1,0 +1,188 @@
+"""fp64 CPU oracle for paged-KV grouped-query attention.
+
+TEST INFRASTRUCTURE ONLY: the parity reference for the HIP kernels.  Only the
+test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with
+``paged_kv_gqa_attention_amd`` and never imports it.
+
+The arithmetic lives in ``pa_oracle.c`` (plain C99, double precision, one row
+at a time).  This module only builds that file with gcc and marshals numpy
+arrays into it.  See ``pa_oracle.h`` for the definition being computed and the
+passages of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "libpa_oracle.so")
+
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc a C source of the oracle into a shared library at ``out``."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra",
+           "-I", _HERE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile pa_oracle.c with gcc into oracle/libpa_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("pt_cols", ctypes.c_int32),
+        ("pt_row_stride", ctypes.c_int32),
+        ("kv_page_stride", ctypes.c_int64),
+        ("q_stride_t", ctypes.c_int64),
+        ("kv_dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+        ("k_descale", ctypes.c_double),
+        ("v_descale", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def load(path: str):
+    """Open a compiled oracle library and declare its signatures."""
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.pao_bf16_to_double.argtypes = [ctypes.c_uint16]
+    L.pao_bf16_to_double.restype = ctypes.c_double
+    L.pao_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    L.pao_fp8_e4m3_to_double.restype = ctypes.c_double
+    L.pao_attention.argtypes = [ctypes.POINTER(Problem), vp, vp, vp, vp, vp, vp,
+                                ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64,
+                                vp, vp, ctypes.c_int]
+    L.pao_attention.restype = ctypes.c_int
+    L.pao_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                            vp, vp, vp, vp]
+    L.pao_merge.restype = ctypes.c_int
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        _lib = load(_LIB)
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().pao_bf16_to_double(int(bits))
+
+
+def fp8_e4m3_to_double(byte: int) -> float:
+    return lib().pao_fp8_e4m3_to_double(int(byte))
+
+
+def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+              page_table: np.ndarray, cu_q_lens: np.ndarray, seq_lens: np.ndarray,
+              num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+              scale: float, causal: bool = True, kv_dtype: int = KV_BF16,
+              k_descale: float = 1.0, v_descale: float = 1.0,
+              rows: Optional[Sequence[int]] = None,
+              key_begin: int = 0, key_end: int = -1,
+              q_stride_t: int = 0, kv_page_stride: int = 0,
+              pt_cols: Optional[int] = None, threads: int = 0):
+    """Reference attention in fp64.
+
+    q_bits   : uint16 bf16 bit patterns, [T, Hq, D] (or a flat buffer with
+               ``q_stride_t`` elements between tokens)
+    k_pool, v_pool : uint16 (bf16 bits) or uint8 (fp8 e4m3 bytes),
+               [P, page, Hkv, D] (or flat with ``kv_page_stride``)
+    page_table : int32 [B, row_stride]; the first ``pt_cols`` columns (default:
+               all) are logical pages, the rest is padding that is never read
+    rows     : None for every (t, h); else flat indices t*Hq + h
+    Returns (out, lse): fp64 [T, Hq, D] and [T, Hq] when rows is None,
+    else [len(rows), D] and [len(rows)].
+    """
+    page_table = _c(page_table, np.int32)
+    if page_table.ndim != 2:
+        raise OracleError("page_table must be 2-D [B, row_stride]")
+    cu_q_lens = _c(cu_q_lens, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    q_bits = _c(q_bits, np.uint16)
+    kv_np = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    k_pool = _c(k_pool, kv_np)
+    v_pool = _c(v_pool, kv_np)
+    B = seq_lens.shape[0]
+    D = head_dim
+    per_page = kv_page_stride if kv_page_stride else page_size * num_kv_heads * D
+    P = k_pool.size // per_page
+    pr = Problem(num_seqs=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                 head_dim=D, page_size=page_size, num_pages=P,
+                 pt_cols=page_table.shape[1] if pt_cols is None else pt_cols,
+                 pt_row_stride=page_table.shape[1],
+                 kv_page_stride=kv_page_stride, q_stride_t=q_stride_t,
+                 kv_dtype=kv_dtype, causal=1 if causal else 0, scale=scale,
+                 k_descale=k_descale, v_descale=v_descale)
+    T = int(cu_q_lens[B]) if B else 0
+    if rows is None:
+        rows_arr = None
+        n = T * num_q_heads
+        out = np.zeros((T, num_q_heads, D), np.float64)
+        lse = np.zeros((T, num_q_heads), np.float64)
+    else:
+        rows_arr = _c(rows, np.int64)
+        n = rows_arr.size
+        out = np.zeros((n, D), np.float64)
+        lse = np.zeros((n,), np.float64)
+    rc = lib().pao_attention(ctypes.byref(pr), _ptr(q_bits), _ptr(k_pool), _ptr(v_pool),
+                             _ptr(page_table), _ptr(cu_q_lens), _ptr(seq_lens),
+                             int(key_begin), int(key_end), _ptr(rows_arr), int(n),
+                             _ptr(out), _ptr(lse), int(threads))
+    if rc != 0:
+        raise OracleError("pao_attention failed with code %d" % rc)
+    return out, lse
+
+
+def merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Combine partials over disjoint key windows: o_parts [S, n, D], lse_parts [S, n]."""
+    o_parts = _c(o_parts, np.float64)
+    lse_parts = _c(lse_parts, np.float64)
+    S, n, D = o_parts.shape
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros((n,), np.float64)
+    rc = lib().pao_merge(S, n, D, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse))
+    if rc != 0:
+        raise OracleError("pao_merge failed with code %d" % rc)
+    return o, lse

@@ -1,0 +1,122 @@
+"""Shared test helpers: workload marshalling and independent reference checks.
+
+Nothing here is imported by the product package or by the oracle.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_gqa_attention_amd import synth
+
+
+def bits(w: synth.Workload):
+    """numpy views of a workload: q bf16 bits, K/V pools (bf16 bits or fp8 bytes)."""
+    q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if w.kv_dtype == "bf16":
+        k = w.k_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
+        v = w.v_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
+    else:
+        k = w.k_pool.contiguous().numpy()
+        v = w.v_pool.contiguous().numpy()
+    return q, k, v
+
+
+def run_oracle(w: synth.Workload, rows=None, key_begin=0, key_end=-1, causal=None,
+               scale=None, threads=0):
+    q, k, v = bits(w)
+    return oracle.attention(
+        q_bits=q, k_pool=k, v_pool=v, page_table=w.page_table.numpy(),
+        cu_q_lens=w.cu_q_lens.numpy(), seq_lens=w.seq_lens.numpy(),
+        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+        page_size=w.page_size, scale=w.scale if scale is None else scale,
+        causal=w.causal if causal is None else causal,
+        kv_dtype=oracle.KV_BF16 if w.kv_dtype == "bf16" else oracle.KV_FP8_E4M3,
+        k_descale=w.k_descale, v_descale=w.v_descale, rows=rows,
+        key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads)
+
+
+def decoded_pools(w: synth.Workload):
+    """K/V pools as float64 tensors, decoded with torch's own dtype casts."""
+    if w.kv_dtype == "bf16":
+        return w.k_pool.to(torch.float64), w.v_pool.to(torch.float64)
+    k = w.k_pool.view(torch.float8_e4m3fn).to(torch.float64) * w.k_descale
+    v = w.v_pool.view(torch.float8_e4m3fn).to(torch.float64) * w.v_descale
+    return k, v
+
+
+def contiguous_kv(w: synth.Workload, b: int, kpool=None, vpool=None):
+    """K and V of sequence b as contiguous [L, Hkv, D] float64, gathered with
+    one fancy-index per tensor (no per-key loop)."""
+    if kpool is None:
+        kpool, vpool = decoded_pools(w)
+    L = int(w.seq_lens[b])
+    j = torch.arange(L)
+    phys = w.page_table[b].to(torch.int64)[j // w.page_size]
+    slot = j % w.page_size
+    return kpool[phys, slot], vpool[phys, slot]
+
+
+def library_attention(w: synth.Workload, causal=None, scale=None):
+    """Attention through torch's CPU flash-attention operator in float64.
+
+    Each sequence's K/V is gathered to a contiguous layout, KV heads are
+    expanded to query heads with repeat_interleave (contiguous groups), and
+    the causal mask is the bottom-right aligned one (query i of a q_len chunk
+    sees keys j <= L - q_len + i).  Returns O [T, Hq, D] and LSE [T, Hq].
+    """
+    causal = w.causal if causal is None else causal
+    scale = w.scale if scale is None else scale
+    kpool, vpool = decoded_pools(w)
+    G = w.num_q_heads // w.num_kv_heads
+    cu = w.cu_q_lens.numpy()
+    T, Hq, D = w.q.shape
+    out = torch.zeros(T, Hq, D, dtype=torch.float64)
+    lse = torch.full((T, Hq), -math.inf, dtype=torch.float64)
+    op = torch.ops.aten._scaled_dot_product_flash_attention_for_cpu
+    for b in range(w.num_seqs):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        ql, L = hi - lo, int(w.seq_lens[b])
+        if ql == 0:
+            continue
+        k, v = contiguous_kv(w, b, kpool, vpool)                   # [L, Hkv, D]
+        qb = w.q[lo:hi].to(torch.float64).permute(1, 0, 2)[None]   # [1, Hq, ql, D]
+        kb = k.permute(1, 0, 2).repeat_interleave(G, dim=0)[None].contiguous()
+        vb = v.permute(1, 0, 2).repeat_interleave(G, dim=0)[None].contiguous()
+        if causal and ql == L:
+            o, l = op(qb, kb, vb, 0.0, True, scale=scale)
+        else:
+            i = torch.arange(ql)[:, None]
+            j = torch.arange(L)[None, :]
+            vis = (j <= (L - ql + i)) if causal else torch.ones(ql, L, dtype=torch.bool)
+            mask = torch.where(vis, 0.0, -math.inf).to(torch.float64)
+            o, l = op(qb, kb, vb, 0.0, False, attn_mask=mask, scale=scale)
+        out[lo:hi] = o[0].permute(1, 0, 2)
+        lse[lo:hi] = l[0].permute(1, 0)
+    return out.numpy(), lse.numpy()
+
+
+def random_workload(seed: int, *, B=None, D=None, page=None, G=None, Hkv=None,
+                    kv_dtype="bf16", causal=True, max_len=80, decode=False,
+                    poison=True) -> synth.Workload:
+    """A small random workload (varying lengths, chunked prefill and decode rows)."""
+    rng = np.random.default_rng(seed)
+    B = B if B is not None else int(rng.integers(1, 5))
+    D = D if D is not None else int(rng.choice([64, 128, 256]))
+    page = page if page is not None else int(rng.choice([16, 32, 64, 128]))
+    G = G if G is not None else int(rng.choice([1, 2, 4, 8]))
+    Hkv = Hkv if Hkv is not None else int(rng.choice([1, 2, 3]))
+    L = rng.integers(1, max_len + 1, size=B)
+    if decode:
+        ql = np.ones(B, dtype=np.int64)
+    else:
+        ql = np.array([int(rng.integers(0, l + 1)) if rng.random() < 0.5 else int(l)
+                       for l in L])
+        ql[ql == 0] = np.minimum(1, L[ql == 0])
+    return synth.build(name="random%d" % seed, seq_lens=L, q_lens=ql,
+                       num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=page,
+                       seed=1000 + seed, kv_dtype=kv_dtype, causal=causal, poison=poison,
+                       threads=1)
