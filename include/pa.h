@@ -1,0 +1,216 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged-KV grouped-query attention on MI355X (gfx950).
+ *
+ * One operation, three schedules.  Every run computes, for each query token t
+ * and query head h,
+ *
+ *     O[t, h, :] = sum_{j visible} softmax_j(scale * q[t,h] . K_j) * V_j
+ *     LSE[t, h]  = ln sum_{j visible} exp(scale * q[t,h] . K_j)
+ *
+ * over the keys of t's sequence b, gathered through an int32 page table:
+ * logical key j < seq_lens[b] lives in physical page page_table[b][j / page],
+ * slot j % page, KV head g = h / (Hq / Hkv).  Queries are the last q_len_b
+ * tokens of their sequence, so token i of sequence b sits at position
+ * seq_lens[b] - q_len_b + i and, when causal, sees keys j <= that position.
+ * Sources:
+ *   - TensorRT-LLM PR #17399 "integrate PrimTS FMHA kernels", section
+ *     "Unified page-table metadata": int32 fixed row-strided page table [B, C]
+ *     plus live int32 sequence lengths [B]; logical page p of request b is
+ *     block_tables[b, p]; columns past the live page count are never consumed;
+ *     K and V keep their own pool displacement.  Section "Planning,
+ *     preprocessing, and workspace ownership": one plan per batch shape,
+ *     request metadata bound at run time, context needs no scratch, decode
+ *     takes a caller-provided aligned workspace, the split-KV counter is the
+ *     only state that must be reset.  Section "Integration and supported
+ *     scope": page sizes 16/32/64/128, head dims 64/128/256, GQA ratio up to
+ *     32, unsupported requests fail closed so a caller can fall back.
+ *   - vLLM PR #16828 "Unified Triton kernel that doesn't distinguish between
+ *     prefill + decode": one kernel for any query length (varlen, like a
+ *     varlen flash-attention call), GQA query heads packed along the query
+ *     dimension, masks applied by selecting -inf.
+ *   - vLLM PR #48156 "[Perf][FA4] Warm up dense (paged) FA4 attention
+ *     kernels": paged prefill/decode specialisations keyed on query-tile
+ *     stage and split-KV (num_splits 0 = heuristic), fp8 KV with descale and
+ *     a bf16 output.
+ *
+ * Conventions
+ *   Ownership   The caller owns every device buffer, the workspace included.
+ *               The library allocates no device memory.  A plan is a host
+ *               object owned by the caller (pa_plan_destroy).
+ *   Streams     pa_run_* enqueue kernels on the given stream and return; they
+ *               never synchronise, allocate, or read device memory on the host,
+ *               so they may be captured into a HIP graph.  Metadata (page table,
+ *               lengths, cu_q_lens, descales) is read by the kernels when they
+ *               run, so a captured graph replays against the current contents.
+ *   Concurrency A plan is immutable after pa_plan and may be shared by threads.
+ *               Runs that overlap in time need distinct workspaces.
+ *   Errors      Host-checkable problems return PA_ERR_INVALID (null or
+ *               misaligned pointers, bad strides, missing fp8 descale),
+ *               PA_ERR_WORKSPACE (workspace smaller than pa_workspace_bytes),
+ *               PA_ERR_UNSUPPORTED (geometry outside the compiled scope: fail
+ *               closed) or PA_ERR_HIP (a launch failed).  Nothing is enqueued
+ *               when a run returns an error.  Device-side contract violations
+ *               (q_len_b > seq_lens[b], seq_lens[b] > C * page, a live page id
+ *               outside [0, num_pages), cu_q_lens[B] > max_total_q) are the
+ *               caller's responsibility; lengths are clamped so the kernels
+ *               stay inside the buffers, page ids are not checked.
+ *   Layouts     All element strides are in elements, not bytes.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* bad argument: null/misaligned pointer, bad stride or size */
+  PA_ERR_UNSUPPORTED = -2,  /* geometry outside the compiled scope (fail closed) */
+  PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than pa_workspace_bytes() */
+  PA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} pa_status;
+
+typedef enum {
+  PA_KV_BF16 = 0,           /* K/V pools hold bfloat16 */
+  PA_KV_FP8_E4M3 = 1        /* K/V pools hold OCP FP8 E4M3 bytes, value = e4m3 * descale */
+} pa_kv_dtype;
+
+/*
+ * Shape bounds of a plan (host values only).
+ *   num_seqs              B: sequences per run (page-table rows, seq_lens entries)
+ *   num_q_heads           Hq; num_kv_heads Hkv; Hq % Hkv == 0, G = Hq/Hkv in {1,2,4,8,16,32}
+ *   head_dim              D in {64, 128, 256}
+ *   page_size             tokens per page, in {16, 32, 64, 128}
+ *   num_pages             P: physical pages in each pool (bounds the page ids)
+ *   page_table_cols       C: logical pages per sequence; seq_lens[b] <= C * page_size
+ *   page_table_row_stride elements between page-table rows, >= C (e.g. 2C for the
+ *                         K plane of a [B, 2, C] table)
+ *   kv_page_stride        elements between consecutive physical pages of a pool;
+ *                         0 means page_size * Hkv * D (dense pool)
+ *   max_total_q           upper bound on total query tokens T = cu_q_lens[B]
+ *   max_q_len             upper bound on any q_len_b (1 for decode)
+ *   max_seq_len           upper bound on any seq_lens[b] (used by the split heuristic;
+ *                         0 means C * page_size)
+ *   kv_dtype              pa_kv_dtype
+ *   num_splits            split-KV factor for decode and mixed runs; 0 = heuristic
+ *   num_cus               compute units to plan for; 0 = query the current device
+ *                         (>0 lets plans be built without a GPU)
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t page_table_cols;
+  int32_t page_table_row_stride;
+  int64_t kv_page_stride;
+  int32_t max_total_q;
+  int32_t max_q_len;
+  int32_t max_seq_len;
+  int32_t kv_dtype;
+  int32_t num_splits;
+  int32_t num_cus;
+} pa_desc;
+
+typedef struct pa_plan_s* pa_plan_t;
+
+/*
+ * Per-run arguments (device pointers unless stated).
+ *   q             bf16 [T, Hq, D], head_dim contiguous, 16-byte aligned
+ *   q_stride_t    elements between consecutive tokens of q (0 = Hq*D); multiple of 8
+ *   k_pool,v_pool [P, page_size, Hkv, D] of kv_dtype, 16-byte aligned, with
+ *                 kv_page_stride elements between pages
+ *   page_table    int32 [B, page_table_row_stride]; row b's first
+ *                 ceil(seq_lens[b] / page_size) entries are read, nothing else
+ *   cu_q_lens     int32 [B+1], cu_q_lens[0] = 0, non-decreasing.  Optional for
+ *                 pa_run_decode (NULL means token b belongs to sequence b).
+ *   seq_lens      int32 [B], live key count per sequence (0 allowed)
+ *   softmax_scale host float multiplying q.k
+ *   causal        host flag: 1 = bottom-right aligned causal mask, 0 = none
+ *   k_descale, v_descale  device fp32 scalars; required for PA_KV_FP8_E4M3 and
+ *                 ignored for PA_KV_BF16
+ *   out           bf16 [T, Hq, D], 16-byte aligned
+ *   o_stride_t    elements between consecutive tokens of out (0 = Hq*D); multiple of 8
+ *   lse           fp32 [T, Hq] natural-log LSE, or NULL to skip.  Rows with no
+ *                 visible key get O = 0 and LSE = -inf.
+ *   workspace     device scratch of at least pa_workspace_bytes(plan) bytes,
+ *                 256-byte aligned; may be NULL when that size is 0
+ */
+typedef struct {
+  const void* q;
+  int64_t q_stride_t;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* cu_q_lens;
+  const int32_t* seq_lens;
+  float softmax_scale;
+  int32_t causal;
+  const float* k_descale;
+  const float* v_descale;
+  void* out;
+  int64_t o_stride_t;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_args;
+
+/* What a plan chose (for tests and benchmarks). */
+typedef struct {
+  int32_t num_splits;        /* split-KV factor used by decode and mixed runs */
+  int32_t split_keys;        /* keys per split window (multiple of the key tile) */
+  int32_t q_block_tokens;    /* query tokens per work item of prefill/mixed runs */
+  int32_t group;             /* G = Hq / Hkv */
+  int32_t num_cus;           /* compute units planned for */
+  int32_t reserved;
+  size_t workspace_bytes;    /* = pa_workspace_bytes(plan) */
+} pa_plan_info;
+
+/* Validate a shape description and build a plan.  Host only; uses the HIP
+ * runtime only when desc->num_cus == 0.  Returns PA_ERR_INVALID for malformed
+ * descriptions and PA_ERR_UNSUPPORTED for geometry outside the compiled scope;
+ * *out is set only on PA_OK. */
+pa_status pa_plan(const pa_desc* desc, pa_plan_t* out);
+
+/* Bytes of workspace a run of this plan needs (0 when no split is used).
+ * Prefill runs need none; decode and mixed runs need this much when the plan
+ * splits the key range. Returns 0 for a NULL plan. */
+size_t pa_workspace_bytes(pa_plan_t plan);
+
+/* Fill *info with the plan's choices. */
+pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info);
+
+/* Varlen prefill (any q_len_b <= seq_lens[b], including chunked prefill on
+ * cached keys): query heads of one KV head packed into bf16 MFMA tiles, K/V
+ * tiles shared through LDS, online softmax.  Never splits the key range and
+ * needs no workspace. */
+pa_status pa_run_prefill(pa_plan_t plan, const pa_args* args, hipStream_t stream);
+
+/* Decode: exactly one query token per sequence (T = B).  Split-KV over the
+ * plan's num_splits windows, then a log-sum-exp merge pass when splits > 1. */
+pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream);
+
+/* Unified mixed batch: any mix of q_len_b in one main launch.  Short rows
+ * (q_len_b * G <= 32) take the decode schedule, longer ones the prefill
+ * schedule, both inside the same kernel; split-KV and the merge pass as for
+ * decode. */
+pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream);
+
+/* Release a plan (NULL is ignored). */
+void pa_plan_destroy(pa_plan_t plan);
+
+/* Static string naming a status code. */
+const char* pa_status_str(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

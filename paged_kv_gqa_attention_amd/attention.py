@@ -1,0 +1,93 @@
+"""Thin torch-facing wrapper over the C ABI: device buffers, plan, workspace, runs.
+
+Nothing here computes attention; it allocates outputs and the workspace with
+torch and calls pa_run_prefill / pa_run_decode / pa_run_mixed of libpa.so.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+class DeviceInputs:
+    """Device copies of a workload's tensors (q, pools, page table, lengths, descales)."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.device = torch.device(device)
+        self.q = w.q.to(self.device)
+        self.k_pool = w.k_pool.to(self.device)
+        self.v_pool = w.v_pool.to(self.device)
+        self.page_table = w.page_table.to(self.device)
+        self.cu_q_lens = w.cu_q_lens.to(self.device)
+        self.seq_lens = w.seq_lens.to(self.device)
+        self.fp8 = w.kv_dtype == "fp8_e4m3"
+        if self.fp8:
+            self.k_descale = torch.tensor([w.k_descale], dtype=torch.float32, device=self.device)
+            self.v_descale = torch.tensor([w.v_descale], dtype=torch.float32, device=self.device)
+        else:
+            self.k_descale = self.v_descale = None
+
+
+class PagedAttention:
+    """A plan for one workload shape plus its workspace."""
+
+    def __init__(self, w, *, num_splits: int = 0, num_cus: int = 0, device="cuda",
+                 max_total_q: Optional[int] = None, max_seq_len: Optional[int] = None):
+        self.w = w
+        self.device = torch.device(device)
+        kv = B.PA_KV_FP8_E4M3 if w.kv_dtype == "fp8_e4m3" else B.PA_KV_BF16
+        self.desc = B.make_desc(
+            num_seqs=w.num_seqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+            head_dim=w.head_dim, page_size=w.page_size, num_pages=w.num_pages,
+            page_table_cols=w.pt_cols, page_table_row_stride=int(w.page_table.shape[1]),
+            max_total_q=w.total_q if max_total_q is None else max_total_q,
+            max_q_len=w.max_q_len,
+            max_seq_len=w.max_seq_len if max_seq_len is None else max_seq_len,
+            kv_dtype=kv, num_splits=num_splits, num_cus=num_cus)
+        self.plan = B.pa_plan(self.desc)
+        self.info = B.pa_plan_get_info(self.plan)
+        nbytes = B.pa_workspace_bytes(self.plan)
+        self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                          if nbytes else None)
+        if self.workspace is not None and self.workspace.data_ptr() % 256:
+            raise RuntimeError("workspace allocation is not 256-byte aligned")
+
+    def __del__(self):
+        plan = getattr(self, "plan", None)
+        if plan is not None:
+            try:
+                B.pa_plan_destroy(plan)
+            except Exception:
+                pass
+            self.plan = None
+
+    def args(self, x: DeviceInputs, out: torch.Tensor, lse: Optional[torch.Tensor],
+             causal: Optional[bool] = None, scale: Optional[float] = None,
+             workspace: Optional[torch.Tensor] = None):
+        return B.make_args(q=x.q, k_pool=x.k_pool, v_pool=x.v_pool, page_table=x.page_table,
+                           cu_q_lens=x.cu_q_lens, seq_lens=x.seq_lens,
+                           softmax_scale=self.w.scale if scale is None else scale,
+                           causal=self.w.causal if causal is None else causal,
+                           out=out, lse=lse, k_descale=x.k_descale, v_descale=x.v_descale,
+                           workspace=self.workspace if workspace is None else workspace)
+
+    def new_outputs(self, x: DeviceInputs):
+        T, Hq, D = x.q.shape
+        out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=self.device)
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=self.device)
+        return out, lse
+
+    def run(self, mode: str, x: DeviceInputs, out=None, lse=None, stream=None, **kw):
+        """mode in {"prefill", "decode", "mixed"}; returns (out, lse)."""
+        if out is None:
+            out, lse = self.new_outputs(x)
+        a = self.args(x, out, lse, **kw)
+        s = B.current_stream() if stream is None else stream
+        fn = {"prefill": B.pa_run_prefill, "decode": B.pa_run_decode,
+              "mixed": B.pa_run_mixed}[mode]
+        fn(self.plan, a, s)
+        return out, lse

@@ -1,0 +1,271 @@
+// pa_api.cpp -- the C ABI of libpa.so: plan validation, split choice, launches.
+//
+// The plan/run split, the caller-owned workspace and the fail-closed scope
+// follow TensorRT-LLM PR #17399 ("integrate PrimTS FMHA kernels", sections
+// "Planning, preprocessing, and workspace ownership" and "Integration and
+// supported scope"); num_splits = 0 meaning "choose by heuristic" follows the
+// split-KV discussion of vLLM PR #48156 ("[Perf][FA4] Warm up dense (paged)
+// FA4 attention kernels").  No function here reads device memory, allocates
+// device memory or synchronises a stream.
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kMaxGroupCols = 32;         // packed query rows per wave
+constexpr int kWavesPerBlock = 8;
+constexpr int kSplitAlign = 64;           // split windows are whole 64-key tiles
+constexpr int kMinSplitKeys = 1024;       // do not split below this many keys per window
+constexpr size_t kWsAlign = 256;
+
+int ilog2(int64_t x) { int s = 0; while ((int64_t(1) << s) < x) ++s; return s; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct pa_plan_s {
+  pa_desc d;
+  int32_t group;
+  int32_t page_shift;
+  int32_t esz;
+  int32_t num_splits;
+  int32_t split_keys;
+  int32_t q_block_tokens;
+  int32_t num_cus;
+  int32_t rows_cap;          // token rows the partial buffers are laid out for
+  int64_t kv_page_bytes;
+  size_t part_o_bytes;
+  size_t ws_bytes;
+};
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID: return "PA_ERR_INVALID: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: geometry outside the supported scope";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown pa_status";
+}
+
+pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
+  if (!desc || !out) return PA_ERR_INVALID;
+  const pa_desc& d = *desc;
+  if (d.num_seqs < 0 || d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.head_dim <= 0 ||
+      d.page_size <= 0 || d.num_pages < 0 || d.page_table_cols < 0 ||
+      d.page_table_row_stride < d.page_table_cols || d.kv_page_stride < 0 ||
+      d.max_total_q < 0 || d.max_q_len < 0 || d.max_seq_len < 0 || d.num_splits < 0 ||
+      d.num_cus < 0)
+    return PA_ERR_INVALID;
+  if (d.num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID;
+  if (d.kv_dtype != PA_KV_BF16 && d.kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  // compiled scope (fail closed)
+  if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32)) return PA_ERR_UNSUPPORTED;
+  if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (d.page_size != 16 && d.page_size != 32 && d.page_size != 64 && d.page_size != 128)
+    return PA_ERR_UNSUPPORTED;
+  const int esz = d.kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
+  const int64_t dense_page = (int64_t)d.page_size * d.num_kv_heads * d.head_dim;
+  const int64_t page_elems = d.kv_page_stride ? d.kv_page_stride : dense_page;
+  if (page_elems < dense_page || (page_elems * esz) % 16 != 0) return PA_ERR_INVALID;
+  const int64_t capacity = (int64_t)d.page_table_cols * d.page_size;
+  if (capacity > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (d.max_seq_len > capacity) return PA_ERR_INVALID;
+
+  int cus = d.num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return PA_ERR_HIP;
+    if (cus <= 0) return PA_ERR_HIP;
+  }
+
+  pa_plan_s* p = new (std::nothrow) pa_plan_s;
+  if (!p) return PA_ERR_INVALID;
+  p->d = d;
+  p->group = G;
+  p->page_shift = ilog2(d.page_size);
+  p->esz = esz;
+  p->num_cus = cus;
+  p->q_block_tokens = std::max(1, kMaxGroupCols * kWavesPerBlock / G);
+  p->kv_page_bytes = page_elems * esz;
+  p->rows_cap = std::max(d.max_total_q, d.num_seqs);
+
+  // Split-KV factor.  Work items of a decode/mixed launch: one per (q-block,
+  // KV head).  Split until there are about four workgroups per compute unit,
+  // but never into windows shorter than kMinSplitKeys keys.
+  const int64_t max_len = d.max_seq_len ? d.max_seq_len : capacity;
+  int splits = d.num_splits;
+  if (splits == 0) {
+    const int64_t qblocks = std::max<int64_t>(1, ceil_div(d.max_total_q, p->q_block_tokens));
+    const int64_t items = std::max<int64_t>(1, std::max<int64_t>(d.num_seqs, qblocks)) * d.num_kv_heads;
+    const int64_t want = ceil_div(4 * (int64_t)cus, items);
+    const int64_t by_len = std::max<int64_t>(1, max_len / kMinSplitKeys);
+    splits = (int)std::max<int64_t>(1, std::min(want, by_len));
+  }
+  int64_t split_keys = capacity > 0 ? ceil_div(capacity, splits) : kSplitAlign;
+  split_keys = std::max<int64_t>(kSplitAlign, ceil_div(split_keys, kSplitAlign) * kSplitAlign);
+  splits = (int)std::max<int64_t>(1, capacity > 0 ? ceil_div(capacity, split_keys) : 1);
+  p->num_splits = splits;
+  p->split_keys = (int32_t)split_keys;
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * (size_t)p->rows_cap * (size_t)d.num_q_heads;
+    p->part_o_bytes = align_up(rows * (size_t)d.head_dim * sizeof(float), kWsAlign);
+    p->ws_bytes = p->part_o_bytes + align_up(rows * sizeof(float), kWsAlign);
+  } else {
+    p->part_o_bytes = 0;
+    p->ws_bytes = 0;
+  }
+  *out = p;
+  return PA_OK;
+}
+
+size_t pa_workspace_bytes(pa_plan_t plan) { return plan ? plan->ws_bytes : 0; }
+
+pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info) {
+  if (!plan || !info) return PA_ERR_INVALID;
+  std::memset(info, 0, sizeof(*info));
+  info->num_splits = plan->num_splits;
+  info->split_keys = plan->split_keys;
+  info->q_block_tokens = plan->q_block_tokens;
+  info->group = plan->group;
+  info->num_cus = plan->num_cus;
+  info->workspace_bytes = plan->ws_bytes;
+  return PA_OK;
+}
+
+void pa_plan_destroy(pa_plan_t plan) { delete plan; }
+
+}  // extern "C"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Host-side checks shared by the three runs; fills the kernel parameters.
+pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_splits,
+                  pa::AttnParams* kp) {
+  if (!plan || !a) return PA_ERR_INVALID;
+  const pa_desc& d = plan->d;
+  const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
+  const int64_t row = (int64_t)d.num_q_heads * d.head_dim;
+  const int64_t q_stride = a->q_stride_t ? a->q_stride_t : row;
+  const int64_t o_stride = a->o_stride_t ? a->o_stride_t : row;
+  if (d.num_seqs > 0) {
+    if (!a->q || !a->k_pool || !a->v_pool || !a->page_table || !a->seq_lens || !a->out)
+      return PA_ERR_INVALID;
+    if (mode != pa::kDecode && !a->cu_q_lens) return PA_ERR_INVALID;
+    if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->out))
+      return PA_ERR_INVALID;
+    if (fp8 && (!a->k_descale || !a->v_descale)) return PA_ERR_INVALID;
+  }
+  if (q_stride < row || o_stride < row || q_stride % 8 || o_stride % 8) return PA_ERR_INVALID;
+  if (!(a->softmax_scale == a->softmax_scale)) return PA_ERR_INVALID;   // NaN scale
+  const bool split = use_splits && plan->num_splits > 1;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (split) {
+    if (!a->workspace || a->workspace_bytes < plan->ws_bytes) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & (kWsAlign - 1)) != 0) return PA_ERR_INVALID;
+    part_o = static_cast<float*>(a->workspace);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan->part_o_bytes);
+  }
+  pa::AttnParams& p = *kp;
+  std::memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_stride_t = q_stride;
+  p.k_pool = static_cast<const uint8_t*>(a->k_pool);
+  p.v_pool = static_cast<const uint8_t*>(a->v_pool);
+  p.kv_page_bytes = plan->kv_page_bytes;
+  p.page_table = a->page_table;
+  p.pt_row_stride = d.page_table_row_stride;
+  p.pt_cols = d.page_table_cols;
+  p.cu_q_lens = a->cu_q_lens;
+  p.seq_lens = a->seq_lens;
+  p.num_seqs = d.num_seqs;
+  p.num_q_heads = d.num_q_heads;
+  p.num_kv_heads = d.num_kv_heads;
+  p.group = plan->group;
+  p.page_shift = plan->page_shift;
+  p.causal = a->causal ? 1 : 0;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.k_descale = fp8 ? a->k_descale : nullptr;
+  p.v_descale = fp8 ? a->v_descale : nullptr;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.o_stride_t = o_stride;
+  p.lse = a->lse;
+  p.num_splits = split ? plan->num_splits : 1;
+  p.split_keys = split ? plan->split_keys : INT32_MAX / 2;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.max_total_q = plan->rows_cap;
+  p.q_block_tokens = plan->q_block_tokens;
+  return PA_OK;
+}
+
+pa_status launch(pa_plan_t plan, const pa::AttnParams& p, pa::Mode mode, hipStream_t stream) {
+  const pa_desc& d = plan->d;
+  if (d.num_seqs == 0) return PA_OK;
+  dim3 grid;
+  if (mode == pa::kDecode) {
+    grid = dim3((unsigned)d.num_seqs, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
+  } else {
+    const int64_t blocks = (int64_t)plan->rows_cap / plan->q_block_tokens + d.num_seqs;
+    grid = dim3((unsigned)blocks, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
+  }
+  const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
+  if (pa::launch_attention(d.head_dim, fp8, mode, p, grid, stream) != hipSuccess) return PA_ERR_HIP;
+  if (p.num_splits > 1) {
+    pa::MergeParams m;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.num_splits = p.num_splits;
+    m.max_total_q = p.max_total_q;
+    m.num_q_heads = d.num_q_heads;
+    m.cu_q_lens = p.cu_q_lens;
+    m.num_seqs = d.num_seqs;
+    m.out = p.out;
+    m.o_stride_t = p.o_stride_t;
+    m.lse = p.lse;
+    if (pa::launch_merge(d.head_dim, m, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+pa_status run(pa_plan_t plan, const pa_args* args, hipStream_t stream, pa::Mode mode) {
+  pa::AttnParams p;
+  const pa_status st = prepare(plan, args, mode, mode != pa::kPrefill, &p);
+  if (st != PA_OK) return st;
+  return launch(plan, p, mode, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_run_prefill(pa_plan_t plan, const pa_args* args, hipStream_t stream) {
+  return run(plan, args, stream, pa::kPrefill);
+}
+
+pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream) {
+  if (plan && plan->d.max_q_len > 1) return PA_ERR_INVALID;
+  return run(plan, args, stream, pa::kDecode);
+}
+
+pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream) {
+  return run(plan, args, stream, pa::kMixed);
+}
+
+}  // extern "C"

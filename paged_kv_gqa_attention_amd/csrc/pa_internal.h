@@ -1,0 +1,75 @@
+// pa_internal.h -- parameters shared by the host side of libpa.so and its HIP kernels.
+#ifndef PA_INTERNAL_H
+#define PA_INTERNAL_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace pa {
+
+// Which work decomposition a launch uses.
+//   kDecode : one query token per sequence; grid (B, Hkv, splits); the waves of a
+//             workgroup split the key range of one (sequence, KV head, split).
+//   kPrefill: grid (q-block bound, Hkv, 1); the waves split the query rows of a
+//             q-block and share K/V tiles through LDS.
+//   kMixed  : grid (q-block bound, Hkv, splits); each q-block picks the decode
+//             schedule when its rows fit one wave (q_len * G <= 32), else the
+//             prefill schedule.
+enum Mode : int { kDecode = 0, kPrefill = 1, kMixed = 2 };
+
+struct AttnParams {
+  const uint16_t* q;            // bf16 bits [T, Hq, D]
+  int64_t q_stride_t;           // elements between tokens
+  const uint8_t* k_pool;        // raw element bytes
+  const uint8_t* v_pool;
+  int64_t kv_page_bytes;        // bytes between physical pages
+  const int32_t* page_table;    // [B, pt_row_stride]
+  int32_t pt_row_stride;
+  int32_t pt_cols;              // C; live keys are clamped to C * page
+  const int32_t* cu_q_lens;     // [B+1]; NULL for decode (token b = sequence b)
+  const int32_t* seq_lens;      // [B]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;                // G = Hq / Hkv
+  int32_t page_shift;           // log2(page size)
+  int32_t causal;
+  float scale_log2;             // softmax_scale * log2(e)
+  const float* k_descale;       // fp8 only (device scalar)
+  const float* v_descale;
+  uint16_t* out;                // bf16 bits [T, Hq, D]
+  int64_t o_stride_t;
+  float* lse;                   // fp32 [T, Hq] natural log, or NULL
+  int32_t num_splits;           // > 1: write partials, merged by merge_kernel
+  int32_t split_keys;           // keys per split window (multiple of 64)
+  float* part_o;                // [S][max_total_q][Hq][D]
+  float* part_lse;              // [S][max_total_q][Hq], log2 units
+  int32_t max_total_q;          // rows at or past this token index are not computed
+  int32_t q_block_tokens;       // tokens per q-block (prefill / mixed)
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_lse;
+  int32_t num_splits;
+  int32_t max_total_q;
+  int32_t num_q_heads;
+  const int32_t* cu_q_lens;     // NULL: total rows = num_seqs (decode)
+  int32_t num_seqs;
+  uint16_t* out;
+  int64_t o_stride_t;
+  float* lse;
+};
+
+// Launch the attention kernel instance for (head_dim, kv dtype, mode).
+hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnParams& p,
+                            dim3 grid, hipStream_t stream);
+// Launch the split-KV log-sum-exp merge.
+hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream);
+// Dynamic LDS bytes the attention instance needs (host-side check).
+int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode);
+
+}  // namespace pa
+
+#endif  // PA_INTERNAL_H

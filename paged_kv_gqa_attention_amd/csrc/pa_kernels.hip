@@ -1,0 +1,796 @@
+// pa_kernels.hip -- paged-KV grouped-query attention kernels for gfx950 (MI355X).
+//
+// One kernel template covers prefill, decode and mixed batches.  The math per
+// (query row, key) pair is the varlen masked-softmax attention of vLLM PR
+// #16828 ("Unified Triton kernel that doesn't distinguish between prefill +
+// decode": any query length in one kernel, GQA heads packed along the query
+// dimension, masked scores selected to -inf), over a KV cache resolved through
+// the int32 page table and live seq_lens of TensorRT-LLM PR #17399
+// ("integrate PrimTS FMHA kernels", section "Unified page-table metadata").
+// The split-KV decode with a log-sum-exp reduction follows the split-KV
+// specialisation discussed in vLLM PR #48156 ("[Perf][FA4] Warm up dense
+// (paged) FA4 attention kernels"); fp8 KV is dequantised with a descale and
+// written out in bf16 as that page describes.
+//
+// gfx950 design
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     K rows are the A operand (32 keys), the packed query rows (up to 32 =
+//     tokens x GQA heads) are the B operand.  The 32x32 accumulator then holds,
+//     in each lane, 16 keys of ONE query row, so the row max and row sum are a
+//     per-lane reduction plus one exchange with lane^32, the running rescale
+//     factor is a per-lane scalar, and the probabilities P^T are already in the
+//     B-operand layout of the second product O^T += V^T P^T (no shuffle of P).
+//   * V^T (head_dim x keys) is produced while staging V into LDS: each lane
+//     loads 16-byte rows of several consecutive keys and writes them back
+//     transposed, so the PV A-operand is two 8-byte (bf16) / 4-byte (fp8) LDS
+//     reads per MFMA.
+//   * fp8 e4m3 K/V stay fp8 in LDS and are widened to bf16 in registers right
+//     before each MFMA with v_cvt_scalef32_pk_bf16_fp8 (exact: e4m3 is a subset
+//     of bf16); k_descale is folded into the score scale, v_descale into the
+//     epilogue.
+//   * Decode schedule: the waves of a workgroup take interleaved 32-key
+//     sub-tiles of one (sequence, KV head, split), each wave staging its own
+//     sub-tile through a private LDS region with register prefetch of the next
+//     one, and the per-wave softmax states are merged through LDS at the end.
+//   * Prefill schedule: each wave owns 32 packed query rows; 64-key K/V tiles
+//     are loaded cooperatively into LDS (register prefetch of the next tile)
+//     and read by every wave; causal sub-tiles above a wave's diagonal are
+//     skipped, and only diagonal/tail sub-tiles are masked.
+//   * Slots past seq_lens[b] are never loaded (zero-filled instead), page-table
+//     columns past the live page count are never read, and masked scores are
+//     selected to -inf, so poisoned cache contents cannot leak into outputs.
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
+constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
+constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
+constexpr int kLdsMax = 160 * 1024;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+template <int A, int B>
+struct CMax { static constexpr int value = A > B ? A : B; };
+
+// Byte geometry of one (head_dim, kv dtype) instance.
+template <int D, bool FP8>
+struct Geo {
+  static constexpr int esz = FP8 ? 1 : 2;              // bytes per K/V element
+  static constexpr int row_bytes = D * esz;            // one token's row of one KV head
+  static constexpr int chunks = row_bytes / 16;        // 16-byte chunks per row
+  static constexpr int elems_per_chunk = 16 / esz;
+  static constexpr int k_pitch = row_bytes + 16;       // LDS bytes per staged K row
+  static constexpr int q_pitch = D * 2 + 16;           // LDS bytes per staged Q row
+  static constexpr int vt_pad = FP8 ? 8 : 16;
+  // decode schedule: per-wave 32-key stage; K rows, then V^T rows, in one region
+  static constexpr int dec_keys_per_lane = (kSub * chunks) / kWave;   // >= 1
+  static constexpr int vt_pitch_sub = kSub * esz + vt_pad;
+  static constexpr int stage_bytes = CMax<kSub * k_pitch, D * vt_pitch_sub>::value;
+  static constexpr int q_bytes = kCols * q_pitch;
+  static constexpr int dec_waves = (kWaves * stage_bytes + q_bytes <= kLdsMax) ? kWaves : kWaves / 2;
+  static constexpr bool dec_prefetch = chunks <= 16;   // keep staging registers <= 64 VGPRs
+  // prefill schedule: 64-key tile, K and V^T resident together
+  static constexpr int pre_keys_per_unit = (kTile * chunks) / kThreads > 0 ? (kTile * chunks) / kThreads : 1;
+  static constexpr int pre_units = (kTile * chunks) / pre_keys_per_unit;
+  static constexpr int vt_pitch_tile = kTile * esz + vt_pad;
+  static constexpr int tile_k_bytes = kTile * k_pitch;
+  static constexpr int tile_bytes = tile_k_bytes + D * vt_pitch_tile;
+  // per-wave softmax state exchanged at the end of the decode schedule
+  static constexpr int red_floats = D / 2 + 2;         // acc registers + l + m, per lane
+  static constexpr int red_bytes = red_floats * kWave * 4;
+};
+
+template <int D, bool FP8, int MODE>
+struct Lds {
+  using G = Geo<D, FP8>;
+  static constexpr int dec = G::q_bytes + G::dec_waves * G::stage_bytes;
+  static constexpr int pre = G::tile_bytes;
+  static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
+  static constexpr int meta = 64;                      // work-item metadata words
+  static constexpr int bytes = base + meta;
+  static_assert(bytes <= kLdsMax, "LDS budget exceeded");
+};
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 fp8 e4m3 bytes (two dwords) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
+  return r;
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, kWave); }
+
+// ---------------------------------------------------------------------------
+// K / V staging: a "unit" is NK consecutive keys x one 16-byte chunk of their rows
+// ---------------------------------------------------------------------------
+
+// Byte offset of (key, kv head g) in a pool, or -1 when the key is not live.
+struct PageWalk {
+  const int32_t* pt_row;   // page-table row of the sequence
+  int64_t page_bytes;      // bytes between physical pages
+  int64_t head_off;        // g * row_bytes
+  int32_t row_stride_b;    // Hkv * row_bytes (bytes between slots of a page)
+  int32_t shift;           // log2(page)
+  int32_t klimit;          // live keys (clamped to C * page)
+};
+
+template <int NK>
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ pool, const PageWalk& w,
+                                          int key0, int chunk, u32x4 (&r)[NK]) {
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int key = key0 + i;
+    if (key < w.klimit) {
+      const int64_t page = __ldg(w.pt_row + (key >> w.shift));
+      const int slot = key & ((1 << w.shift) - 1);
+      const uint8_t* src = pool + page * w.page_bytes + (int64_t)slot * w.row_stride_b + w.head_off +
+                           chunk * 16;
+      r[i] = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      r[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// K rows: key (kbase + i) at row pitch, chunk offset.
+template <int NK, int PITCH>
+__device__ __forceinline__ void store_k(uint8_t* kl, int krow0, int chunk, const u32x4 (&r)[NK]) {
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    *reinterpret_cast<u32x4*>(kl + (krow0 + i) * PITCH + chunk * 16) = r[i];
+}
+
+// V^T: element e of the chunk is row d = chunk * elems + e; the NK keys are
+// consecutive columns starting at key column kcol0.
+template <int NK, bool FP8, int PITCH>
+__device__ __forceinline__ void store_vt(uint8_t* vt, int kcol0, int chunk, const u32x4 (&r)[NK]) {
+  constexpr int esz = FP8 ? 1 : 2;
+  constexpr int E = 16 / esz;
+  constexpr int bytes = NK * esz;             // bytes written per d row
+  constexpr int words = bytes >= 4 ? bytes / 4 : 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint8_t* dst = vt + (chunk * E + e) * PITCH + kcol0 * esz;
+    uint32_t wv[words];
+#pragma unroll
+    for (int k = 0; k < words; ++k) wv[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      uint32_t val;
+      if (FP8)
+        val = (r[i][e >> 2] >> (8 * (e & 3))) & 0xFFu;
+      else
+        val = (r[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const int bit = i * esz * 8;
+      wv[bit >> 5] |= val << (bit & 31);
+    }
+    if constexpr (bytes == 1) {
+      *dst = (uint8_t)wv[0];
+    } else if constexpr (bytes == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wv[0];
+    } else if constexpr (bytes == 4) {
+      *reinterpret_cast<uint32_t*>(dst) = wv[0];
+    } else if constexpr (bytes == 8) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < words; k += 4)
+        *reinterpret_cast<u32x4*>(dst + 4 * k) = u32x4{wv[k], wv[k + 1], wv[k + 2], wv[k + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// one 32-key score tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct SoftmaxState {
+  f32x16 o[D / 32];   // O^T tiles: reg i of tile t <-> d = 32t + (i/4)*8 + (lane/32)*4 + i%4
+  float m;            // running max of scaled scores (log2 units), per query row
+  float l;            // running sum of exp2(score - m), this lane's 16 keys of each tile
+};
+
+template <int D>
+__device__ __forceinline__ void state_init(SoftmaxState<D>& st) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[t][i] = 0.f;
+  st.m = neg_inf();
+  st.l = 0.f;
+}
+
+// K operand for k-step j: K[key = kb + lane%32][d = 16j + (lane/32)*8 .. +8]
+template <int D, bool FP8, int KPITCH>
+__device__ __forceinline__ bf16x8 k_operand(const uint8_t* kl, int kb, int j, int lane) {
+  const uint8_t* src = kl + (kb + (lane & 31)) * KPITCH + (16 * j + (lane >> 5) * 8) * (FP8 ? 1 : 2);
+  if constexpr (FP8) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(src);
+    return fp8x8_to_bf16(w[0], w[1]);
+  } else {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+  }
+}
+
+// V^T operand for d-tile t and k-step s of the tile whose keys start at
+// column kb: rows d = 32t + lane%32, keys kb + 16s + (lane/32)*4 + {0..3} and
+// kb + 16s + 8 + (lane/32)*4 + {0..3} -- the keys lane holds in P^T.
+template <bool FP8, int VTPITCH>
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vt, int kb, int t, int s, int lane) {
+  const uint8_t* row = vt + (32 * t + (lane & 31)) * VTPITCH;
+  const int k = kb + 16 * s + (lane >> 5) * 4;
+  if constexpr (FP8) {
+    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(row + k);
+    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(row + k + 8);
+    return fp8x8_to_bf16(w0, w1);
+  } else {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(row + 2 * k);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(row + 2 * (k + 8));
+    return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+  }
+}
+
+// Scores of one 32-key tile into s (raw q.k, fp32).
+template <int D, bool FP8, int KPITCH, bool QLDS>
+__device__ __forceinline__ f32x16 score_tile(const uint8_t* kl, int kb, const bf16x8* qreg,
+                                             const uint8_t* ql, int qpitch, int lane) {
+  f32x16 s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const bf16x8 a = k_operand<D, FP8, KPITCH>(kl, kb, j, lane);
+    bf16x8 bq;
+    if constexpr (QLDS)
+      bq = as_bf16x8(*reinterpret_cast<const u32x4*>(ql + (lane & 31) * qpitch + (16 * j + (lane >> 5) * 8) * 2));
+    else
+      bq = qreg[j];
+    s = mfma32(a, bq, s);
+  }
+  return s;
+}
+
+// Online softmax update and PV for one tile.  c = scale * log2(e) (* k_descale);
+// key0 = absolute key of the tile's first row; klim = this lane's query row
+// sees keys < klim (only consulted when MASK).
+template <int D, bool FP8, int VTPITCH, bool MASK>
+__device__ __forceinline__ void softmax_pv(SoftmaxState<D>& st, f32x16 s, float c, int key0,
+                                           int klim, const uint8_t* vt, int kb, int lane) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    x[i] = s[i] * c;
+    if (MASK) {
+      const int key = key0 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      x[i] = key < klim ? x[i] : neg_inf();
+    }
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  mx = fmaxf(mx, xor32(mx));
+  const float m_new = fmaxf(st.m, mx);
+  // m_new == -inf: nothing visible yet; use 0 as the reference so that
+  // exp2(-inf - 0) = 0 everywhere instead of NaN.
+  const float ref = m_new == neg_inf() ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
+  float p[16];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(x[i] - ref);
+    psum += p[i];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = m_new;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
+  const bf16x8 p0 = pack_bf16x8(p);
+  const bf16x8 p1 = pack_bf16x8(p + 8);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    st.o[t] = mfma32(v_operand<FP8, VTPITCH>(vt, kb, t, 0, lane), p0, st.o[t]);
+    st.o[t] = mfma32(v_operand<FP8, VTPITCH>(vt, kb, t, 1, lane), p1, st.o[t]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// output
+// ---------------------------------------------------------------------------
+
+struct RowMap {
+  int t0;       // absolute token index of the block's first query token
+  int ntok;     // query tokens in the block
+  int pos0;     // absolute position of the first token in its sequence
+  int g;        // KV head
+  int G;        // query heads per KV head
+};
+
+// Write one wave's 32 query rows (columns) starting at packed row r0.  l is
+// already the full row sum (both lane halves).
+template <int D>
+__device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float l_tot, int r0,
+                           const RowMap& rm, int split, float vdesc, int lane) {
+  const int r = r0 + (lane & 31);
+  const int tok = r / rm.G;
+  if (tok >= rm.ntok) return;
+  const int t = rm.t0 + tok;
+  if (t >= p.max_total_q) return;
+  const int h = rm.g * rm.G + (r - tok * rm.G);
+  const bool empty = !(l_tot > 0.f);
+  const float inv = empty ? 0.f : vdesc / l_tot;
+  const float lse2 = empty ? neg_inf() : st.m + __builtin_amdgcn_logf(l_tot);  // v_log_f32 is log2
+  if (p.num_splits > 1) {
+    const int64_t row = ((int64_t)split * p.max_total_q + t) * p.num_q_heads + h;
+    if ((lane >> 5) == 0) p.part_lse[row] = lse2;
+    if (empty) return;
+    float* dst = p.part_o + row * D;
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
+        f32x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = st.o[tt][4 * ig + k] * inv;
+        *reinterpret_cast<f32x4*>(dst + d0) = v;
+      }
+  } else {
+    uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D;
+#pragma unroll
+    for (int tt = 0; tt < D / 32; ++tt)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
+        const u32x2 v{pack_bf16x2(st.o[tt][4 * ig] * inv, st.o[tt][4 * ig + 1] * inv),
+                      pack_bf16x2(st.o[tt][4 * ig + 2] * inv, st.o[tt][4 * ig + 3] * inv)};
+        *reinterpret_cast<u32x2*>(dst + d0) = v;
+      }
+    if (p.lse && (lane >> 5) == 0) p.lse[(int64_t)t * p.num_q_heads + h] = lse2 * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode schedule: waves split the key range of one block of <= 32 query rows
+// ---------------------------------------------------------------------------
+
+template <int D, bool FP8>
+__device__ void keysplit_item(const AttnParams& p, uint8_t* smem, const RowMap& rm,
+                              const PageWalk& pw, int L, int split, float c, float vdesc) {
+  using Gm = Geo<D, FP8>;
+  constexpr int NW = Gm::dec_waves;
+  constexpr int NK = Gm::dec_keys_per_lane;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int nrows = rm.ntok * rm.G;
+
+  // stage the block's query rows (zero padded to 32) in LDS
+  uint8_t* ql = smem;
+  {
+    constexpr int cpr = D * 2 / 16;
+    for (int u = threadIdx.x; u < kCols * cpr; u += kThreads) {
+      const int r = u / cpr, ch = u % cpr;
+      u32x4 v{0u, 0u, 0u, 0u};
+      if (r < nrows) {
+        const int tok = r / rm.G;
+        const int h = rm.g * rm.G + (r - tok * rm.G);
+        v = *reinterpret_cast<const u32x4*>(p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t +
+                                            (int64_t)h * D + ch * 8);
+      }
+      *reinterpret_cast<u32x4*>(ql + r * Gm::q_pitch + ch * 16) = v;
+    }
+  }
+  __syncthreads();
+
+  // key window of this split, clipped by the causal limit of the last token
+  const int klo = split * p.split_keys;
+  int khi = min(L, klo + p.split_keys);
+  if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
+  const int nsub = khi > klo ? (khi - klo + kSub - 1) / kSub : 0;
+  // this lane's query row sees keys < klim
+  const int my_tok = min((lane & 31) / rm.G, max(rm.ntok - 1, 0));
+  const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
+  // keys below kfull are visible to every row of the block
+  const int kfull = p.causal ? min(khi, rm.pos0 + 1) : khi;
+
+  SoftmaxState<D> st;
+  state_init(st);
+
+  if (wave < NW) {
+    uint8_t* stage = smem + Gm::q_bytes + wave * Gm::stage_bytes;
+    const int chunk = lane % Gm::chunks;
+    const int kg = lane / Gm::chunks;      // key group of this lane
+    u32x4 kr[NK], vr[NK];
+    int n = wave;
+    if (Gm::dec_prefetch && n < nsub) {
+      load_unit<NK>(p.k_pool, pw, klo + n * kSub + kg * NK, chunk, kr);
+      load_unit<NK>(p.v_pool, pw, klo + n * kSub + kg * NK, chunk, vr);
+    }
+    for (; n < nsub; n += NW) {
+      const int key0 = klo + n * kSub;
+      const bool has_next = n + NW < nsub;
+      if (!Gm::dec_prefetch) load_unit<NK>(p.k_pool, pw, key0 + kg * NK, chunk, kr);
+      store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
+      if (Gm::dec_prefetch && has_next) load_unit<NK>(p.k_pool, pw, key0 + NW * kSub + kg * NK, chunk, kr);
+      __builtin_amdgcn_wave_barrier();
+      const f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
+      __builtin_amdgcn_wave_barrier();
+      if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, pw, key0 + kg * NK, chunk, vr);
+      store_vt<NK, FP8, Gm::vt_pitch_sub>(stage, kg * NK, chunk, vr);
+      if (Gm::dec_prefetch && has_next) load_unit<NK>(p.v_pool, pw, key0 + NW * kSub + kg * NK, chunk, vr);
+      __builtin_amdgcn_wave_barrier();
+      if (key0 + kSub <= kfull)
+        softmax_pv<D, FP8, Gm::vt_pitch_sub, false>(st, s, c, key0, klim, stage, 0, lane);
+      else
+        softmax_pv<D, FP8, Gm::vt_pitch_sub, true>(st, s, c, key0, klim, stage, 0, lane);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  // merge the per-wave states pairwise through LDS: (m, l, O) of a writer wave
+  // folded into a reader wave with the usual max-rescale.
+  __syncthreads();
+  constexpr int lds_avail = Lds<D, FP8, kDecode>::base;
+  constexpr int nbuf_raw = lds_avail / Gm::red_bytes;
+  constexpr int nbuf = nbuf_raw < 1 ? 1 : nbuf_raw;
+  static_assert(nbuf_raw >= 1, "no LDS for the wave merge");
+  float* red = reinterpret_cast<float*>(smem);
+  int active = NW;
+  while (active > 1) {
+    const int half = active / 2;
+    const int cnt = half < nbuf ? half : nbuf;
+    const int w_lo = active - cnt;         // writers [w_lo, active)
+    const int r_lo = active - 2 * cnt;     // readers [r_lo, w_lo)
+    if (wave >= w_lo && wave < active) {
+      float* buf = red + (wave - w_lo) * Gm::red_floats * kWave;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) buf[(t * 16 + i) * kWave + lane] = st.o[t][i];
+      buf[(D / 2) * kWave + lane] = st.l;
+      buf[(D / 2 + 1) * kWave + lane] = st.m;
+    }
+    __syncthreads();
+    if (wave >= r_lo && wave < w_lo) {
+      const float* buf = red + (wave - r_lo) * Gm::red_floats * kWave;
+      const float l2 = buf[(D / 2) * kWave + lane];
+      const float m2 = buf[(D / 2 + 1) * kWave + lane];
+      const float mm = fmaxf(st.m, m2);
+      const float ref = mm == neg_inf() ? 0.f : mm;
+      const float a1 = __builtin_amdgcn_exp2f(st.m - ref);
+      const float a2 = __builtin_amdgcn_exp2f(m2 - ref);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[t][i] = st.o[t][i] * a1 + buf[(t * 16 + i) * kWave + lane] * a2;
+      st.l = st.l * a1 + l2 * a2;
+      st.m = mm;
+    }
+    __syncthreads();
+    active = w_lo;
+  }
+  if (wave == 0) {
+    const float l_tot = st.l + xor32(st.l);
+    write_rows<D>(p, st, l_tot, 0, rm, split, vdesc, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill schedule: each wave owns 32 packed query rows; K/V tiles shared in LDS
+// ---------------------------------------------------------------------------
+
+template <int D, bool FP8>
+__device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, const RowMap& rm,
+                              const PageWalk& pw, int L, int split, float c, float vdesc) {
+  using Gm = Geo<D, FP8>;
+  constexpr int NK = Gm::pre_keys_per_unit;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int nrows = rm.ntok * rm.G;
+  const int r0 = wave * kCols;               // this wave's first packed row
+
+  // Q operand for this wave's rows, in registers
+  bf16x8 qreg[D / 16];
+  {
+    const int r = r0 + (lane & 31);
+    const bool ok = r < nrows;
+    const int tok = ok ? r / rm.G : 0;
+    const int h = rm.g * rm.G + (r - tok * rm.G);
+    const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j))
+                   : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+
+  const int klo = split * p.split_keys;
+  int khi = min(L, klo + p.split_keys);
+  if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
+  const int ntiles = khi > klo ? (khi - klo + kTile - 1) / kTile : 0;
+
+  // wave-level visibility: rows of this wave are tokens [tok_a, tok_b]
+  const bool wave_active = r0 < nrows;
+  const int tok_a = min(r0 / rm.G, max(rm.ntok - 1, 0));
+  const int tok_b = min((r0 + kCols - 1) / rm.G, max(rm.ntok - 1, 0));
+  const int wave_kmax = p.causal ? min(khi, rm.pos0 + tok_b + 1) : khi;   // no key >= this is visible
+  const int wave_kfull = p.causal ? min(khi, rm.pos0 + tok_a + 1) : khi;  // keys < this visible to all
+  const int my_tok = min((r0 + (lane & 31)) / rm.G, max(rm.ntok - 1, 0));
+  const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
+
+  SoftmaxState<D> st;
+  state_init(st);
+
+  uint8_t* kl = smem;
+  uint8_t* vt = smem + Gm::tile_k_bytes;
+  const int unit = threadIdx.x;
+  const bool loader = unit < Gm::pre_units;
+  const int chunk = unit % Gm::chunks;
+  const int kg = unit / Gm::chunks;
+  u32x4 kr[NK], vr[NK];
+  if (loader && ntiles > 0) {
+    load_unit<NK>(p.k_pool, pw, klo + kg * NK, chunk, kr);
+    load_unit<NK>(p.v_pool, pw, klo + kg * NK, chunk, vr);
+  }
+  for (int tix = 0; tix < ntiles; ++tix) {
+    const int key0 = klo + tix * kTile;
+    __syncthreads();
+    if (loader) {
+      store_k<NK, Gm::k_pitch>(kl, kg * NK, chunk, kr);
+      store_vt<NK, FP8, Gm::vt_pitch_tile>(vt, kg * NK, chunk, vr);
+    }
+    __syncthreads();
+    if (loader && tix + 1 < ntiles) {
+      load_unit<NK>(p.k_pool, pw, key0 + kTile + kg * NK, chunk, kr);
+      load_unit<NK>(p.v_pool, pw, key0 + kTile + kg * NK, chunk, vr);
+    }
+    if (wave_active) {
+#pragma unroll
+      for (int sb = 0; sb < kTile / kSub; ++sb) {
+        const int k0 = key0 + sb * kSub;
+        if (k0 < wave_kmax) {
+          const f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
+          if (k0 + kSub <= wave_kfull)
+            softmax_pv<D, FP8, Gm::vt_pitch_tile, false>(st, s, c, k0, klim, vt, sb * kSub, lane);
+          else
+            softmax_pv<D, FP8, Gm::vt_pitch_tile, true>(st, s, c, k0, klim, vt, sb * kSub, lane);
+        }
+      }
+    }
+  }
+  if (wave_active) {
+    const float l_tot = st.l + xor32(st.l);
+    write_rows<D>(p, st, l_tot, r0, rm, split, vdesc, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel: work-item decode, then one of the two schedules
+// ---------------------------------------------------------------------------
+
+template <int D, bool FP8, int MODE>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
+  int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
+  const int g = blockIdx.y;
+  const int split = blockIdx.z;
+  int b, t0, ntok, q_len, i0 = 0;
+  if constexpr (MODE == kDecode) {
+    b = blockIdx.x;
+    if (p.cu_q_lens) {
+      t0 = p.cu_q_lens[b];
+      q_len = p.cu_q_lens[b + 1] - t0;
+      ntok = min(q_len, 1);
+    } else {
+      t0 = b;
+      q_len = 1;
+      ntok = 1;
+    }
+  } else {
+    // Work item -> (sequence, q-block).  Sequence b owns the block indices
+    // [cu[b]/BQ + b, cu[b]/BQ + b + ceil(q_len_b/BQ)), which never overlap
+    // and stay below cu[B]/BQ + B, so the grid can be sized from host bounds.
+    const int BQ = p.q_block_tokens;
+    const int x = blockIdx.x;
+    if (threadIdx.x == 0) meta[0] = 0;
+    __syncthreads();
+    int cnt = 0;
+    for (int j = threadIdx.x; j < p.num_seqs; j += kThreads) cnt += (p.cu_q_lens[j] / BQ + j <= x) ? 1 : 0;
+    if (cnt) atomicAdd(&meta[0], cnt);
+    __syncthreads();
+    b = meta[0] - 1;
+    if (b < 0) return;
+    t0 = p.cu_q_lens[b];
+    q_len = p.cu_q_lens[b + 1] - t0;
+    const int local = x - (t0 / BQ + b);
+    i0 = local * BQ;
+    if (i0 >= q_len) return;
+    ntok = min(BQ, q_len - i0);
+    t0 += i0;
+  }
+  if (ntok <= 0) {
+    // no query row in this block; nothing to write
+    return;
+  }
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  RowMap rm;
+  rm.t0 = t0;
+  rm.ntok = ntok;
+  // position of the block's first token: the queries are the last q_len keys
+  rm.pos0 = L - q_len + i0;
+  rm.g = g;
+  rm.G = p.group;
+  PageWalk pw;
+  pw.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
+  pw.page_bytes = p.kv_page_bytes;
+  pw.head_off = (int64_t)g * Geo<D, FP8>::row_bytes;
+  pw.row_stride_b = p.num_kv_heads * Geo<D, FP8>::row_bytes;
+  pw.shift = p.page_shift;
+  pw.klimit = L;
+  float c = p.scale_log2;
+  float vdesc = 1.f;
+  if (FP8) {
+    c *= *p.k_descale;
+    vdesc = *p.v_descale;
+  }
+  if constexpr (MODE == kDecode) {
+    keysplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+  } else if constexpr (MODE == kPrefill) {
+    rowsplit_item<D, FP8>(p, smem, rm, pw, L, 0, c, vdesc);
+  } else {
+    if (q_len * p.group <= kCols)
+      keysplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+    else
+      rowsplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV merge: LSE = log sum exp(LSE_s), O = sum exp(LSE_s - LSE) O_s
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // t * Hq + h
+  const int total_t = p.cu_q_lens ? p.cu_q_lens[p.num_seqs] : p.num_seqs;
+  const int64_t nrows = (int64_t)min(total_t, p.max_total_q) * p.num_q_heads;
+  if (row >= nrows) return;
+  const int t = (int)(row / p.num_q_heads);
+  const int h = (int)(row - (int64_t)t * p.num_q_heads);
+  const int64_t plane = (int64_t)p.max_total_q * p.num_q_heads;
+  float mx = neg_inf();
+  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.part_lse[s * plane + row]);
+  constexpr int PER = D / 64;     // d values per lane
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float wsum = 0.f;
+  if (mx != neg_inf()) {
+    for (int s = 0; s < p.num_splits; ++s) {
+      const float ls = p.part_lse[s * plane + row];
+      if (ls == neg_inf()) continue;
+      const float w = __builtin_amdgcn_exp2f(ls - mx);
+      wsum += w;
+      const float* src = p.part_o + (s * plane + row) * D + lane * PER;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + lane * PER;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const __bf16 v = (__bf16)(acc[k] * inv);
+    dst[k] = __builtin_bit_cast(uint16_t, v);
+  }
+  if (p.lse && lane == 0)
+    p.lse[row] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+}
+
+template <int D, bool FP8, int MODE>
+hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool FP8>
+hipError_t launch_mode(Mode mode, const AttnParams& p, dim3 grid, hipStream_t stream) {
+  switch (mode) {
+    case kDecode: return launch_one<D, FP8, kDecode>(p, grid, stream);
+    case kPrefill: return launch_one<D, FP8, kPrefill>(p, grid, stream);
+    case kMixed: return launch_one<D, FP8, kMixed>(p, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, bool FP8>
+int lds_mode(Mode mode) {
+  switch (mode) {
+    case kDecode: return Lds<D, FP8, kDecode>::bytes;
+    case kPrefill: return Lds<D, FP8, kPrefill>::bytes;
+    case kMixed: return Lds<D, FP8, kMixed>::bytes;
+  }
+  return 0;
+}
+
+}  // namespace
+
+hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnParams& p, dim3 grid,
+                            hipStream_t stream) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: return kv_fp8 ? launch_mode<64, true>(mode, p, grid, stream) : launch_mode<64, false>(mode, p, grid, stream);
+    case 128: return kv_fp8 ? launch_mode<128, true>(mode, p, grid, stream) : launch_mode<128, false>(mode, p, grid, stream);
+    case 256: return kv_fp8 ? launch_mode<256, true>(mode, p, grid, stream) : launch_mode<256, false>(mode, p, grid, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
+  switch (head_dim) {
+    case 64: return kv_fp8 ? lds_mode<64, true>(mode) : lds_mode<64, false>(mode);
+    case 128: return kv_fp8 ? lds_mode<128, true>(mode) : lds_mode<128, false>(mode);
+    case 256: return kv_fp8 ? lds_mode<256, true>(mode) : lds_mode<256, false>(mode);
+  }
+  return 0;
+}
+
+hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.max_total_q * p.num_q_heads;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (grid.x == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa
