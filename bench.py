@@ -1,0 +1,238 @@
+"""Benchmark: paged-KV GQA attention on one MI355X.
+
+Headline line: the decode workload (B=256, Hq/Hkv 32/8, D 128, page 16,
+seq_lens U[1024, 2048], bf16 K/V) through pa_run_decode, reported as KV GB/s
+and as a fraction of the 8 TB/s HBM3E roof.  The other full-size workloads
+(causal varlen prefill, unified mixed batch, fp8 long-context decode) are
+timed too and reported under "secondary".  Every workload is validated
+against the fp64 oracle on sampled rows before it is timed.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu]
+
+One "step" is one call of the entry point over the whole batch (all kernels
+of the call, the split-KV merge included), inputs already resident in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn prefill TFLOP/s + decode KV GB/s, as % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_attention_amd", "csrc", "pa_kernels.hip")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+O_TOL = {"bf16": 1.5e-2, "fp8_e4m3": 6e-2}
+LSE_TOL = 1e-3
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None when absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, "%s_counters.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_sha:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_bytes or m_sha.group(1) != kernel_sha():
+        return None
+    return float(m_bytes.group(1))
+
+
+def validate(w, out, lse, rows, oracle_rows):
+    o = out.float().cpu().numpy().reshape(-1, w.head_dim)[rows].astype(np.float64)
+    l = lse.float().cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    ro, rl = oracle_rows
+    eo = float(np.max(np.abs(o - ro)))
+    el = float(np.max(np.abs(l - rl)))
+    ok = bool(np.all(np.isfinite(o)) and eo <= O_TOL[w.kv_dtype] and el <= LSE_TOL)
+    return ok, eo, el
+
+
+def time_steps(fn, steps: int, warmup: int, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps       # ms per step
+
+
+def bench_workload(name, mode, steps, warmup, sample_rows_per_seq=2, heads=2):
+    """Generate, validate on sampled rows, time.  Returns a result dict."""
+    import torch
+    from paged_kv_gqa_attention_amd import synth
+    from paged_kv_gqa_attention_amd.attention import DeviceInputs, PagedAttention
+    from tests import helpers as H
+
+    t0 = time.time()
+    w = synth.WORKLOADS[name]()
+    gen_s = time.time() - t0
+    x = DeviceInputs(w)
+    pa = PagedAttention(w)
+    out, lse = pa.new_outputs(x)
+    stream = torch.cuda.current_stream()
+    args = pa.args(x, out, lse)
+    from paged_kv_gqa_attention_amd import binding as B
+    run = {"prefill": B.pa_run_prefill, "decode": B.pa_run_decode, "mixed": B.pa_run_mixed}[mode]
+    s_ptr = int(stream.cuda_stream)
+
+    def step():
+        run(pa.plan, args, s_ptr)
+
+    step()
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, per_seq=sample_rows_per_seq, heads=heads)
+    ok, eo, el = validate(w, out, lse, rows, H.run_oracle(w, rows=rows))
+    ms = time_steps(step, steps, warmup, stream)
+    kv = w.kv_bytes()
+    qo = w.qo_bytes()
+    flops = w.flops()
+    res = {
+        "workload": name, "entry": "pa_run_" + mode, "ms_per_step": ms,
+        "kv_bytes": kv, "qo_bytes": qo, "flops": flops,
+        "kv_gbs": kv / (ms * 1e-3) / 1e9,
+        "alg_gbs": (kv + qo) / (ms * 1e-3) / 1e9,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "num_splits": int(pa.info.num_splits),
+        "validated_rows": len(rows), "max_abs_err_o": eo, "max_abs_err_lse": el,
+        "valid": ok, "gen_s": round(gen_s, 2), "w": w,
+    }
+    return res
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample: whole sequences (all heads) in
+    order until about budget_s seconds of work; reports KV GB/s over the sample."""
+    from tests import helpers as H
+    Hq = w.num_q_heads
+    cu = w.cu_q_lens.numpy()
+    L = w.seq_lens.numpy().astype(np.int64)
+    threads = os.cpu_count() or 1
+    done_bytes, elapsed, nseq = 0, 0.0, 0
+    b = 0
+    while b < w.num_seqs and elapsed < budget_s:
+        take = min(w.num_seqs - b, 16)
+        rows = np.arange(cu[b] * Hq, cu[b + take] * Hq, dtype=np.int64)
+        t = time.time()
+        H.run_oracle(w, rows=rows, threads=threads)
+        elapsed += time.time() - t
+        done_bytes += int(L[b:b + take].sum()) * w.num_kv_heads * w.head_dim * 2 * \
+            (2 if w.kv_dtype == "bf16" else 1)
+        nseq += take
+        b += take
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d sequences (all %d query heads), %.1f s of fp64 CPU work"
+                      % (nseq, w.num_seqs, Hq, elapsed)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None, help="time one workload by name and print it")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    modes = {"decode_llama8b": "decode", "prefill_causal": "prefill",
+             "mixed_24b": "mixed", "decode_fp8_long": "decode"}
+
+    def strip(r):
+        return {k: v for k, v in r.items() if k != "w"}
+
+    if a.only:
+        r = bench_workload(a.only, modes[a.only], a.steps, a.warmup)
+        print(json.dumps(strip(r)), flush=True)
+        return
+
+    prim = bench_workload("decode_llama8b", "decode", a.steps, a.warmup)
+    print("# primary validated=%s err_o=%.3g err_lse=%.3g ms=%.4f" % (
+        prim["valid"], prim["max_abs_err_o"], prim["max_abs_err_lse"], prim["ms_per_step"]),
+        file=sys.stderr, flush=True)
+    sec = {}
+    if not a.no_secondary:
+        for name in ("prefill_causal", "mixed_24b", "decode_fp8_long"):
+            r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup)
+            bound = "mfma" if name == "prefill_causal" else "hbm"
+            if bound == "mfma":
+                frac = r["tflops"] / BF16_PEAK_TFLOPS
+            elif name == "mixed_24b":
+                frac = max(r["tflops"] / BF16_PEAK_TFLOPS, r["alg_gbs"] / HBM_PEAK_GBS)
+            else:
+                frac = r["alg_gbs"] / HBM_PEAK_GBS
+            e = strip(r)
+            e["bound"] = bound
+            e["roofline_frac"] = frac
+            sec[name] = e
+            print("# %s validated=%s ms=%.4f frac=%.3f" % (name, r["valid"], r["ms_per_step"], frac),
+                  file=sys.stderr, flush=True)
+    w = prim["w"]
+    alg_bytes = prim["kv_bytes"] + prim["qo_bytes"]
+    achieved = alg_bytes / (prim["ms_per_step"] * 1e-3) / 1e9
+    cpu = None if a.no_cpu else cpu_baseline(w)
+    line = {
+        "metric": METRIC,
+        "value": round(prim["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_llama8b", "entry": "pa_run_decode", "num_seqs": 256,
+                   "num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "page_size": 16,
+                   "seq_lens": "U[1024,2048] seed 2", "kv_dtype": "bf16",
+                   "num_splits": prim["num_splits"], "parallelism": "single GPU"},
+        "valid": prim["valid"],
+        "max_abs_err_o": prim["max_abs_err_o"],
+        "max_abs_err_lse": prim["max_abs_err_lse"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("decode_llama8b"),
+                     "kernel": "attn_kernel<128, bf16, decode>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+        "secondary": sec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
