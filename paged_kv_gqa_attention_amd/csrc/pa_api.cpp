@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kMaxGroupCols = 32;         // packed query rows per wave
 constexpr int kWavesPerBlock = 8;
-constexpr int kSplitAlign = 64;           // split windows are whole 64-key tiles
+constexpr int kSplitAlign = 128;          // split windows: whole 64-key tiles, page aligned
 constexpr int kMinSplitKeys = 1024;       // do not split below this many keys per window
 constexpr size_t kWsAlign = 256;
 

@@ -58,6 +58,7 @@ constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
 constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
 constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
 constexpr int kLdsMax = 160 * 1024;
+constexpr int kPcacheEntries = 1024;      // page ids cached in LDS per chunk of keys
 constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
@@ -100,7 +101,9 @@ struct Lds {
   static constexpr int pre = G::tile_bytes;
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
-  static constexpr int bytes = base + meta;
+  static constexpr int pcache_entries = kPcacheEntries;
+  static constexpr int pcache_off = base + meta;
+  static constexpr int bytes = pcache_off + pcache_entries * 4;
   static_assert(bytes <= kLdsMax, "LDS budget exceeded");
 };
 
@@ -146,31 +149,45 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, kWave
 // K / V staging: a "unit" is NK consecutive keys x one 16-byte chunk of their rows
 // ---------------------------------------------------------------------------
 
-// Byte offset of (key, kv head g) in a pool, or -1 when the key is not live.
+// Where a sequence's K/V rows live.  Page ids of the keys being processed are
+// cached in LDS (pcache[i] = page_table[row][first_page + i]) so that every
+// K/V load can be issued without waiting on a page-table load.
 struct PageWalk {
   const int32_t* pt_row;   // page-table row of the sequence
+  const int32_t* pcache;   // LDS copy of page ids from first_page on
+  int32_t first_page;
   int64_t page_bytes;      // bytes between physical pages
   int64_t head_off;        // g * row_bytes
   int32_t row_stride_b;    // Hkv * row_bytes (bytes between slots of a page)
   int32_t shift;           // log2(page)
   int32_t klimit;          // live keys (clamped to C * page)
+  int32_t kend;            // loads clamp to keys below this: min(chunk end, klimit)
 };
 
+// Copy the page ids of keys [k_begin, k_end) (clamped to live keys) into the
+// LDS cache.  Only columns below ceil(klimit / page) are ever read.
+__device__ __forceinline__ void fill_pcache(PageWalk& w, int32_t* pcache, int k_begin, int k_end) {
+  const int last_key = min(k_end, w.klimit) - 1;
+  w.kend = last_key + 1;
+  w.first_page = k_begin >> w.shift;
+  w.pcache = pcache;
+  const int n = last_key >= k_begin ? (last_key >> w.shift) - w.first_page + 1 : 0;
+  for (int i = threadIdx.x; i < n; i += kThreads) pcache[i] = w.pt_row[w.first_page + i];
+}
+
+// NK consecutive keys from key0, one 16-byte chunk each.  Keys at or past the
+// end of the cached window (never past the live length) are clamped to its
+// last key: they load finite data that the score mask gives probability 0.
 template <int NK>
 __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ pool, const PageWalk& w,
                                           int key0, int chunk, u32x4 (&r)[NK]) {
+  const uint8_t* base = pool + w.head_off + chunk * 16;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
-    const int key = key0 + i;
-    if (key < w.klimit) {
-      const int64_t page = __ldg(w.pt_row + (key >> w.shift));
-      const int slot = key & ((1 << w.shift) - 1);
-      const uint8_t* src = pool + page * w.page_bytes + (int64_t)slot * w.row_stride_b + w.head_off +
-                           chunk * 16;
-      r[i] = *reinterpret_cast<const u32x4*>(src);
-    } else {
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    const int key = min(key0 + i, w.kend - 1);
+    const int64_t page = w.pcache[(key >> w.shift) - w.first_page];
+    const int slot = key & ((1 << w.shift) - 1);
+    r[i] = *reinterpret_cast<const u32x4*>(base + page * w.page_bytes + (int64_t)slot * w.row_stride_b);
   }
 }
 
@@ -400,13 +417,13 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
 // ---------------------------------------------------------------------------
 
 template <int D, bool FP8>
-__device__ void keysplit_item(const AttnParams& p, uint8_t* smem, const RowMap& rm,
+__device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
   constexpr int NW = Gm::dec_waves;
   constexpr int NK = Gm::dec_keys_per_lane;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrows = rm.ntok * rm.G;
 
   // stage the block's query rows (zero padded to 32) in LDS
@@ -431,7 +448,6 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, const RowMap& 
   const int klo = split * p.split_keys;
   int khi = min(L, klo + p.split_keys);
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
-  const int nsub = khi > klo ? (khi - klo + kSub - 1) / kSub : 0;
   // this lane's query row sees keys < klim
   const int my_tok = min((lane & 31) / rm.G, max(rm.ntok - 1, 0));
   const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
@@ -441,34 +457,46 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, const RowMap& 
   SoftmaxState<D> st;
   state_init(st);
 
-  if (wave < NW) {
-    uint8_t* stage = smem + Gm::q_bytes + wave * Gm::stage_bytes;
-    const int chunk = lane % Gm::chunks;
-    const int kg = lane / Gm::chunks;      // key group of this lane
-    u32x4 kr[NK], vr[NK];
-    int n = wave;
-    if (Gm::dec_prefetch && n < nsub) {
-      load_unit<NK>(p.k_pool, pw, klo + n * kSub + kg * NK, chunk, kr);
-      load_unit<NK>(p.v_pool, pw, klo + n * kSub + kg * NK, chunk, vr);
-    }
-    for (; n < nsub; n += NW) {
-      const int key0 = klo + n * kSub;
-      const bool has_next = n + NW < nsub;
-      if (!Gm::dec_prefetch) load_unit<NK>(p.k_pool, pw, key0 + kg * NK, chunk, kr);
-      store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
-      if (Gm::dec_prefetch && has_next) load_unit<NK>(p.k_pool, pw, key0 + NW * kSub + kg * NK, chunk, kr);
-      __builtin_amdgcn_wave_barrier();
-      const f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
-      __builtin_amdgcn_wave_barrier();
-      if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, pw, key0 + kg * NK, chunk, vr);
-      store_vt<NK, FP8, Gm::vt_pitch_sub>(stage, kg * NK, chunk, vr);
-      if (Gm::dec_prefetch && has_next) load_unit<NK>(p.v_pool, pw, key0 + NW * kSub + kg * NK, chunk, vr);
-      __builtin_amdgcn_wave_barrier();
-      if (key0 + kSub <= kfull)
-        softmax_pv<D, FP8, Gm::vt_pitch_sub, false>(st, s, c, key0, klim, stage, 0, lane);
-      else
-        softmax_pv<D, FP8, Gm::vt_pitch_sub, true>(st, s, c, key0, klim, stage, 0, lane);
-      __builtin_amdgcn_wave_barrier();
+  PageWalk w = pw;
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    __syncthreads();
+    const int nsub = (ce - cb + kSub - 1) / kSub;
+    if (wave < NW) {
+      uint8_t* stage = smem + Gm::q_bytes + wave * Gm::stage_bytes;
+      const int chunk = lane % Gm::chunks;
+      const int kg = lane / Gm::chunks;      // key group of this lane
+      u32x4 kr[NK], vr[NK];
+      int n = wave;
+      if (Gm::dec_prefetch && n < nsub) {
+        load_unit<NK>(p.k_pool, w, cb + n * kSub + kg * NK, chunk, kr);
+        load_unit<NK>(p.v_pool, w, cb + n * kSub + kg * NK, chunk, vr);
+      }
+      for (; n < nsub; n += NW) {
+        const int key0 = cb + n * kSub;
+        // Prefetch target: the wave's next sub-tile, or (last iteration) a
+        // sub-tile already in cache.  Unconditional, so that the compiler's
+        // load counters stay exact and no wait covers the prefetch itself.
+        const int key_next = cb + min(n + NW, nsub - 1) * kSub;
+        if (!Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key0 + kg * NK, chunk, kr);
+        store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
+        if (Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
+        __builtin_amdgcn_wave_barrier();
+        const f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        __builtin_amdgcn_wave_barrier();
+        if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key0 + kg * NK, chunk, vr);
+        store_vt<NK, FP8, Gm::vt_pitch_sub>(stage, kg * NK, chunk, vr);
+        if (Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
+        __builtin_amdgcn_wave_barrier();
+        if (key0 + kSub <= kfull)
+          softmax_pv<D, FP8, Gm::vt_pitch_sub, false>(st, s, c, key0, klim, stage, 0, lane);
+        else
+          softmax_pv<D, FP8, Gm::vt_pitch_sub, true>(st, s, c, key0, klim, stage, 0, lane);
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
 
@@ -525,12 +553,12 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, const RowMap& 
 // ---------------------------------------------------------------------------
 
 template <int D, bool FP8>
-__device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, const RowMap& rm,
+__device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
   constexpr int NK = Gm::pre_keys_per_unit;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrows = rm.ntok * rm.G;
   const int r0 = wave * kCols;               // this wave's first packed row
 
@@ -551,8 +579,6 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, const RowMap& 
   const int klo = split * p.split_keys;
   int khi = min(L, klo + p.split_keys);
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
-  const int ntiles = khi > klo ? (khi - klo + kTile - 1) / kTile : 0;
-
   // wave-level visibility: rows of this wave are tokens [tok_a, tok_b]
   const bool wave_active = r0 < nrows;
   const int tok_a = min(r0 / rm.G, max(rm.ntok - 1, 0));
@@ -572,32 +598,44 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, const RowMap& 
   const int chunk = unit % Gm::chunks;
   const int kg = unit / Gm::chunks;
   u32x4 kr[NK], vr[NK];
-  if (loader && ntiles > 0) {
-    load_unit<NK>(p.k_pool, pw, klo + kg * NK, chunk, kr);
-    load_unit<NK>(p.v_pool, pw, klo + kg * NK, chunk, vr);
-  }
-  for (int tix = 0; tix < ntiles; ++tix) {
-    const int key0 = klo + tix * kTile;
+  PageWalk w = pw;
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
     __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    __syncthreads();
+    const int ntiles = (ce - cb + kTile - 1) / kTile;
     if (loader) {
-      store_k<NK, Gm::k_pitch>(kl, kg * NK, chunk, kr);
-      store_vt<NK, FP8, Gm::vt_pitch_tile>(vt, kg * NK, chunk, vr);
+      load_unit<NK>(p.k_pool, w, cb + kg * NK, chunk, kr);
+      load_unit<NK>(p.v_pool, w, cb + kg * NK, chunk, vr);
     }
-    __syncthreads();
-    if (loader && tix + 1 < ntiles) {
-      load_unit<NK>(p.k_pool, pw, key0 + kTile + kg * NK, chunk, kr);
-      load_unit<NK>(p.v_pool, pw, key0 + kTile + kg * NK, chunk, vr);
-    }
-    if (wave_active) {
+    for (int tix = 0; tix < ntiles; ++tix) {
+      const int key0 = cb + tix * kTile;
+      __syncthreads();
+      if (loader) {
+        store_k<NK, Gm::k_pitch>(kl, kg * NK, chunk, kr);
+        store_vt<NK, FP8, Gm::vt_pitch_tile>(vt, kg * NK, chunk, vr);
+      }
+      __syncthreads();
+      if (loader) {
+        // next tile, or (last tile) the current one again: unconditional so the
+        // load counters stay exact across iterations
+        const int key_next = cb + min(tix + 1, ntiles - 1) * kTile;
+        load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
+        load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
+      }
+      if (wave_active) {
 #pragma unroll
-      for (int sb = 0; sb < kTile / kSub; ++sb) {
-        const int k0 = key0 + sb * kSub;
-        if (k0 < wave_kmax) {
-          const f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
-          if (k0 + kSub <= wave_kfull)
-            softmax_pv<D, FP8, Gm::vt_pitch_tile, false>(st, s, c, k0, klim, vt, sb * kSub, lane);
-          else
-            softmax_pv<D, FP8, Gm::vt_pitch_tile, true>(st, s, c, k0, klim, vt, sb * kSub, lane);
+        for (int sb = 0; sb < kTile / kSub; ++sb) {
+          const int k0 = key0 + sb * kSub;
+          if (k0 < wave_kmax) {
+            const f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
+            if (k0 + kSub <= wave_kfull)
+              softmax_pv<D, FP8, Gm::vt_pitch_tile, false>(st, s, c, k0, klim, vt, sb * kSub, lane);
+            else
+              softmax_pv<D, FP8, Gm::vt_pitch_tile, true>(st, s, c, k0, klim, vt, sb * kSub, lane);
+          }
         }
       }
     }
@@ -616,6 +654,7 @@ template <int D, bool FP8, int MODE>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
+  int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
   const int g = blockIdx.y;
   const int split = blockIdx.z;
   int b, t0, ntok, q_len, i0 = 0;
@@ -678,14 +717,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     vdesc = *p.v_descale;
   }
   if constexpr (MODE == kDecode) {
-    keysplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+    keysplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
-    rowsplit_item<D, FP8>(p, smem, rm, pw, L, 0, c, vdesc);
+    rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
     if (q_len * p.group <= kCols)
-      keysplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+      keysplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
     else
-      rowsplit_item<D, FP8>(p, smem, rm, pw, L, split, c, vdesc);
+      rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   }
 }
 
