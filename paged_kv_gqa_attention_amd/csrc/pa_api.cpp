@@ -18,8 +18,6 @@
 
 namespace {
 
-constexpr int kMaxGroupCols = 32;         // packed query rows per wave
-constexpr int kWavesPerBlock = 8;
 constexpr int kSplitAlign = 128;          // split windows: whole 64-key tiles, page aligned
 constexpr int kMinSplitKeys = 1024;       // do not split below this many keys per window
 constexpr size_t kWsAlign = 256;
@@ -99,7 +97,7 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   p->page_shift = ilog2(d.page_size);
   p->esz = esz;
   p->num_cus = cus;
-  p->q_block_tokens = std::max(1, kMaxGroupCols * kWavesPerBlock / G);
+  p->q_block_tokens = std::max(1, pa::prefill_block_rows(d.head_dim) / G);
   p->kv_page_bytes = page_elems * esz;
   p->rows_cap = std::max(d.max_total_q, d.num_seqs);
 

@@ -67,8 +67,10 @@ hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnPara
                             dim3 grid, hipStream_t stream);
 // Launch the split-KV log-sum-exp merge.
 hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream);
-// Dynamic LDS bytes the attention instance needs (host-side check).
+// LDS bytes the attention instance uses (host-side check).
 int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode);
+// Packed query rows (tokens x GQA heads) per prefill/mixed workgroup.
+int prefill_block_rows(int head_dim);
 
 }  // namespace pa
 

@@ -52,8 +52,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kWaves = 8;                 // waves per workgroup, prefill and mixed launches
 constexpr int kThreads = kWave * kWaves;
+constexpr int kDecWaves = 4;              // waves per workgroup, decode launches
+
+// Workgroup shape of a launch.  Decode workgroups are half size so that two
+// of them share a compute unit and one's prologue/epilogue overlaps the
+// other's streaming.  Head dim 256 keeps a 128-row fp32 accumulator per wave,
+// so its workgroups run one wave per SIMD with the accumulator in AGPRs.
+template <int MODE, int D>
+struct Block {
+  static constexpr int waves = (MODE == kDecode || D == 256) ? kDecWaves : kWaves;
+  static constexpr int threads = waves * kWave;
+  static constexpr int waves_per_eu = D == 256 ? 1 : 2;
+};
 constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
 constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
 constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
@@ -81,10 +93,13 @@ struct Geo {
   static constexpr int vt_pitch_sub = kSub * esz + vt_pad;
   static constexpr int stage_bytes = CMax<kSub * k_pitch, D * vt_pitch_sub>::value;
   static constexpr int q_bytes = kCols * q_pitch;
-  static constexpr int dec_waves = (kWaves * stage_bytes + q_bytes <= kLdsMax) ? kWaves : kWaves / 2;
+  // waves of a decode-schedule item that stage K/V (for an NWB-wave workgroup)
+  template <int NWB>
+  struct DecWaves { static constexpr int value = (NWB * stage_bytes + q_bytes <= kLdsMax - 8192) ? NWB : NWB / 2; };
   static constexpr bool dec_prefetch = chunks <= 16;   // keep staging registers <= 64 VGPRs
   // prefill schedule: 64-key tile, K and V^T resident together
-  static constexpr int pre_keys_per_unit = (kTile * chunks) / kThreads > 0 ? (kTile * chunks) / kThreads : 1;
+  static constexpr int pre_threads = Block<kPrefill, D>::threads;
+  static constexpr int pre_keys_per_unit = (kTile * chunks) / pre_threads > 0 ? (kTile * chunks) / pre_threads : 1;
   static constexpr int pre_units = (kTile * chunks) / pre_keys_per_unit;
   static constexpr int vt_pitch_tile = kTile * esz + vt_pad;
   static constexpr int tile_k_bytes = kTile * k_pitch;
@@ -97,7 +112,7 @@ struct Geo {
 template <int D, bool FP8, int MODE>
 struct Lds {
   using G = Geo<D, FP8>;
-  static constexpr int dec = G::q_bytes + G::dec_waves * G::stage_bytes;
+  static constexpr int dec = G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
   static constexpr int pre = G::tile_bytes;
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
@@ -172,7 +187,7 @@ __device__ __forceinline__ void fill_pcache(PageWalk& w, int32_t* pcache, int k_
   w.first_page = k_begin >> w.shift;
   w.pcache = pcache;
   const int n = last_key >= k_begin ? (last_key >> w.shift) - w.first_page + 1 : 0;
-  for (int i = threadIdx.x; i < n; i += kThreads) pcache[i] = w.pt_row[w.first_page + i];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) pcache[i] = w.pt_row[w.first_page + i];
 }
 
 // NK consecutive keys from key0, one 16-byte chunk each.  Keys at or past the
@@ -416,11 +431,12 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
 // decode schedule: waves split the key range of one block of <= 32 query rows
 // ---------------------------------------------------------------------------
 
-template <int D, bool FP8>
+template <int D, bool FP8, int MODE>
 __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
-  constexpr int NW = Gm::dec_waves;
+  constexpr int NWB = Block<MODE, D>::waves;             // waves in the workgroup
+  constexpr int NW = Gm::template DecWaves<NWB>::value;   // waves that stage K/V
   constexpr int NK = Gm::dec_keys_per_lane;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -430,7 +446,7 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   uint8_t* ql = smem;
   {
     constexpr int cpr = D * 2 / 16;
-    for (int u = threadIdx.x; u < kCols * cpr; u += kThreads) {
+    for (int u = threadIdx.x; u < kCols * cpr; u += Block<MODE, D>::threads) {
       const int r = u / cpr, ch = u % cpr;
       u32x4 v{0u, 0u, 0u, 0u};
       if (r < nrows) {
@@ -503,7 +519,7 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   // merge the per-wave states pairwise through LDS: (m, l, O) of a writer wave
   // folded into a reader wave with the usual max-rescale.
   __syncthreads();
-  constexpr int lds_avail = Lds<D, FP8, kDecode>::base;
+  constexpr int lds_avail = Lds<D, FP8, MODE>::base;
   constexpr int nbuf_raw = lds_avail / Gm::red_bytes;
   constexpr int nbuf = nbuf_raw < 1 ? 1 : nbuf_raw;
   static_assert(nbuf_raw >= 1, "no LDS for the wave merge");
@@ -651,7 +667,9 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 // ---------------------------------------------------------------------------
 
 template <int D, bool FP8, int MODE>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__((Block<MODE, D>::threads))
+__attribute__((amdgpu_waves_per_eu(Block<MODE, D>::waves_per_eu, Block<MODE, D>::waves_per_eu)))
+void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
@@ -678,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     if (threadIdx.x == 0) meta[0] = 0;
     __syncthreads();
     int cnt = 0;
-    for (int j = threadIdx.x; j < p.num_seqs; j += kThreads) cnt += (p.cu_q_lens[j] / BQ + j <= x) ? 1 : 0;
+    for (int j = threadIdx.x; j < p.num_seqs; j += Block<MODE, D>::threads) cnt += (p.cu_q_lens[j] / BQ + j <= x) ? 1 : 0;
     if (cnt) atomicAdd(&meta[0], cnt);
     __syncthreads();
     b = meta[0] - 1;
@@ -717,12 +735,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnParams p) {
     vdesc = *p.v_descale;
   }
   if constexpr (MODE == kDecode) {
-    keysplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
+    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
     rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
     if (q_len * p.group <= kCols)
-      keysplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
+      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
     else
       rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   }
@@ -773,7 +791,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 
 template <int D, bool FP8, int MODE>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -815,6 +833,15 @@ int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
     case 64: return kv_fp8 ? lds_mode<64, true>(mode) : lds_mode<64, false>(mode);
     case 128: return kv_fp8 ? lds_mode<128, true>(mode) : lds_mode<128, false>(mode);
     case 256: return kv_fp8 ? lds_mode<256, true>(mode) : lds_mode<256, false>(mode);
+  }
+  return 0;
+}
+
+int prefill_block_rows(int head_dim) {
+  switch (head_dim) {
+    case 64: return Block<kPrefill, 64>::waves * kCols;
+    case 128: return Block<kPrefill, 128>::waves * kCols;
+    case 256: return Block<kPrefill, 256>::waves * kCols;
   }
   return 0;
 }
