@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one workload by name and print it")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -173,6 +175,17 @@ def main():
     def strip(r):
         return {k: v for k, v in r.items() if k != "w"}
 
+    if a.calibrate_copy:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "repeats": 5}), flush=True)
+        return
     if a.only:
         r = bench_workload(a.only, modes[a.only], a.steps, a.warmup)
         print(json.dumps(strip(r)), flush=True)
