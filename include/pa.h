@@ -133,7 +133,9 @@ typedef struct pa_plan_s* pa_plan_t;
  *   cu_q_lens     int32 [B+1], cu_q_lens[0] = 0, non-decreasing.  Optional for
  *                 pa_run_decode (NULL means token b belongs to sequence b).
  *   seq_lens      int32 [B], live key count per sequence (0 allowed)
- *   softmax_scale host float multiplying q.k
+ *   softmax_scale host float multiplying q.k; must be positive and finite
+ *                 (PA_ERR_INVALID otherwise).  For fp8 KV, *k_descale must be
+ *                 positive as well (device value, not checked).
  *   causal        host flag: 1 = bottom-right aligned causal mask, 0 = none
  *   k_descale, v_descale  device fp32 scalars; required for PA_KV_FP8_E4M3 and
  *                 ignored for PA_KV_BF16

@@ -170,7 +170,8 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
     if (fp8 && (!a->k_descale || !a->v_descale)) return PA_ERR_INVALID;
   }
   if (q_stride < row || o_stride < row || q_stride % 8 || o_stride % 8) return PA_ERR_INVALID;
-  if (!(a->softmax_scale == a->softmax_scale)) return PA_ERR_INVALID;   // NaN scale
+  // the kernels fold the scale into exp2 arguments and need it positive and finite
+  if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 3.0e38f)) return PA_ERR_INVALID;
   const bool split = use_splits && plan->num_splits > 1;
   float* part_o = nullptr;
   float* part_lse = nullptr;

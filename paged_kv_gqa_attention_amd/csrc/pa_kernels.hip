@@ -87,11 +87,13 @@ struct Geo {
   static constexpr int elems_per_chunk = 16 / esz;
   static constexpr int k_pitch = row_bytes + 16;       // LDS bytes per staged K row
   static constexpr int q_pitch = D * 2 + 16;           // LDS bytes per staged Q row
-  static constexpr int vt_pad = FP8 ? 8 : 16;
-  // decode schedule: per-wave 32-key stage; K rows, then V^T rows, in one region
+  // V rows are staged row-major like K and read transposed by the LDS unit
+  // (ds_read_b64_tr_b16 / _tr_b8); the extra pad staggers the rows one
+  // transposed read touches across banks.
+  static constexpr int v_pitch = row_bytes + 32;
+  // decode schedule: per-wave 32-key stage; K rows, then V rows, in one region
   static constexpr int dec_keys_per_lane = (kSub * chunks) / kWave;   // >= 1
-  static constexpr int vt_pitch_sub = kSub * esz + vt_pad;
-  static constexpr int stage_bytes = CMax<kSub * k_pitch, D * vt_pitch_sub>::value;
+  static constexpr int stage_bytes = CMax<kSub * k_pitch, kSub * v_pitch>::value;
   static constexpr int q_bytes = kCols * q_pitch;
   // waves of a decode-schedule item that stage K/V (for an NWB-wave workgroup)
   template <int NWB>
@@ -101,9 +103,8 @@ struct Geo {
   static constexpr int pre_threads = Block<kPrefill, D>::threads;
   static constexpr int pre_keys_per_unit = (kTile * chunks) / pre_threads > 0 ? (kTile * chunks) / pre_threads : 1;
   static constexpr int pre_units = (kTile * chunks) / pre_keys_per_unit;
-  static constexpr int vt_pitch_tile = kTile * esz + vt_pad;
   static constexpr int tile_k_bytes = kTile * k_pitch;
-  static constexpr int tile_bytes = tile_k_bytes + D * vt_pitch_tile;
+  static constexpr int tile_bytes = tile_k_bytes + kTile * v_pitch;
   // per-wave softmax state exchanged at the end of the decode schedule
   static constexpr int red_floats = D / 2 + 2;         // acc registers + l + m, per lane
   static constexpr int red_bytes = red_floats * kWave * 4;
@@ -113,7 +114,7 @@ template <int D, bool FP8, int MODE>
 struct Lds {
   using G = Geo<D, FP8>;
   static constexpr int dec = G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
-  static constexpr int pre = G::tile_bytes;
+  static constexpr int pre = 2 * G::tile_bytes;         // double-buffered K / V tiles
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
   static constexpr int pcache_entries = kPcacheEntries;
@@ -206,52 +207,12 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ pool, cons
   }
 }
 
-// K rows: key (kbase + i) at row pitch, chunk offset.
+// K or V rows: key (krow0 + i) at the row pitch, chunk offset.
 template <int NK, int PITCH>
 __device__ __forceinline__ void store_k(uint8_t* kl, int krow0, int chunk, const u32x4 (&r)[NK]) {
 #pragma unroll
   for (int i = 0; i < NK; ++i)
     *reinterpret_cast<u32x4*>(kl + (krow0 + i) * PITCH + chunk * 16) = r[i];
-}
-
-// V^T: element e of the chunk is row d = chunk * elems + e; the NK keys are
-// consecutive columns starting at key column kcol0.
-template <int NK, bool FP8, int PITCH>
-__device__ __forceinline__ void store_vt(uint8_t* vt, int kcol0, int chunk, const u32x4 (&r)[NK]) {
-  constexpr int esz = FP8 ? 1 : 2;
-  constexpr int E = 16 / esz;
-  constexpr int bytes = NK * esz;             // bytes written per d row
-  constexpr int words = bytes >= 4 ? bytes / 4 : 1;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    uint8_t* dst = vt + (chunk * E + e) * PITCH + kcol0 * esz;
-    uint32_t wv[words];
-#pragma unroll
-    for (int k = 0; k < words; ++k) wv[k] = 0u;
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      uint32_t val;
-      if (FP8)
-        val = (r[i][e >> 2] >> (8 * (e & 3))) & 0xFFu;
-      else
-        val = (r[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const int bit = i * esz * 8;
-      wv[bit >> 5] |= val << (bit & 31);
-    }
-    if constexpr (bytes == 1) {
-      *dst = (uint8_t)wv[0];
-    } else if constexpr (bytes == 2) {
-      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wv[0];
-    } else if constexpr (bytes == 4) {
-      *reinterpret_cast<uint32_t*>(dst) = wv[0];
-    } else if constexpr (bytes == 8) {
-      *reinterpret_cast<u32x2*>(dst) = u32x2{wv[0], wv[1]};
-    } else {
-#pragma unroll
-      for (int k = 0; k < words; k += 4)
-        *reinterpret_cast<u32x4*>(dst + 4 * k) = u32x4{wv[k], wv[k + 1], wv[k + 2], wv[k + 3]};
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -275,10 +236,18 @@ __device__ __forceinline__ void state_init(SoftmaxState<D>& st) {
   st.l = 0.f;
 }
 
-// K operand for k-step j: K[key = kb + lane%32][d = 16j + (lane/32)*8 .. +8]
+// Key order inside a 32-key score tile.  MFMA row m of S^T = K Q^T holds key
+// kperm(m) (bits 2 and 3 of m swapped).  With that order, accumulator element
+// i of lane l holds key (i & 7) + 8*(l/32) + 16*(i/8): each lane's probabilities
+// for one PV k-step are 8 CONSECUTIVE keys, which is what the transposing LDS
+// reads below deliver for the V operand.
+__device__ __forceinline__ int kperm(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+__device__ __forceinline__ int acc_key(int i, int lane) { return (i & 7) + 8 * (lane >> 5) + 16 * (i >> 3); }
+
+// K operand for k-step j: K[key = kb + kperm(lane%32)][d = 16j + (lane/32)*8 .. +8]
 template <int D, bool FP8, int KPITCH>
 __device__ __forceinline__ bf16x8 k_operand(const uint8_t* kl, int kb, int j, int lane) {
-  const uint8_t* src = kl + (kb + (lane & 31)) * KPITCH + (16 * j + (lane >> 5) * 8) * (FP8 ? 1 : 2);
+  const uint8_t* src = kl + (kb + kperm(lane & 31)) * KPITCH + (16 * j + (lane >> 5) * 8) * (FP8 ? 1 : 2);
   if constexpr (FP8) {
     const u32x2 w = *reinterpret_cast<const u32x2*>(src);
     return fp8x8_to_bf16(w[0], w[1]);
@@ -287,21 +256,34 @@ __device__ __forceinline__ bf16x8 k_operand(const uint8_t* kl, int kb, int j, in
   }
 }
 
-// V^T operand for d-tile t and k-step s of the tile whose keys start at
-// column kb: rows d = 32t + lane%32, keys kb + 16s + (lane/32)*4 + {0..3} and
-// kb + 16s + 8 + (lane/32)*4 + {0..3} -- the keys lane holds in P^T.
-template <bool FP8, int VTPITCH>
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vt, int kb, int t, int s, int lane) {
-  const uint8_t* row = vt + (32 * t + (lane & 31)) * VTPITCH;
-  const int k = kb + 16 * s + (lane >> 5) * 4;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// V^T operand for d-tile t and k-step s of the tile whose keys start at row kb
+// of a row-major V stage: lane l needs V[kb + 16s + 8*(l/32) + kk][32t + l%32]
+// for kk = 0..7.  Within each 16-lane group the transposing read hands output
+// lane L element L%4 (tr_b16) / byte L%8 (tr_b8) of the 8-byte segments read by
+// a fixed set of source lanes; each source lane below reads the segment that
+// makes output lane L receive consecutive keys of column 32t + (l%32).
+template <bool FP8, int VPITCH>
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* vl, int kb, int t, int s, int lane) {
+  const int L = lane & 15;
+  const int d0 = 32 * t + 16 * ((lane >> 4) & 1);
+  const int k0 = kb + 16 * s + 8 * (lane >> 5);
   if constexpr (FP8) {
-    const uint32_t w0 = *reinterpret_cast<const uint32_t*>(row + k);
-    const uint32_t w1 = *reinterpret_cast<const uint32_t*>(row + k + 8);
-    return fp8x8_to_bf16(w0, w1);
+    // source lane L: key k0 + L/2, columns d0 + 8*(L%2) .. +7
+    const uint8_t* src = vl + (k0 + (L >> 1)) * VPITCH + d0 + 8 * (L & 1);
+    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(src));
+    return fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
   } else {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(row + 2 * k);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(row + 2 * (k + 8));
-    return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+    // source lane L: key k0 + L/4 (+4 for the second read), columns d0 + 4*(L%4) .. +3
+    const uint8_t* src = vl + (k0 + (L >> 2)) * VPITCH + 2 * (d0 + 4 * (L & 3));
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(src + 4 * VPITCH));
+    return as_bf16x8(u32x4{__builtin_bit_cast(u32x2, a)[0], __builtin_bit_cast(u32x2, a)[1],
+                           __builtin_bit_cast(u32x2, b)[0], __builtin_bit_cast(u32x2, b)[1]});
   }
 }
 
@@ -325,49 +307,57 @@ __device__ __forceinline__ f32x16 score_tile(const uint8_t* kl, int kb, const bf
   return s;
 }
 
-// Online softmax update and PV for one tile.  c = scale * log2(e) (* k_descale);
-// key0 = absolute key of the tile's first row; klim = this lane's query row
-// sees keys < klim (only consulted when MASK).
-template <int D, bool FP8, int VTPITCH, bool MASK>
-__device__ __forceinline__ void softmax_pv(SoftmaxState<D>& st, f32x16 s, float c, int key0,
-                                           int klim, const uint8_t* vt, int kb, int lane) {
-  float x[16];
+// Mask the scores of one tile: key index of s[i] in this lane, keys >= klim
+// (this lane's query row) become -inf.  Applied only on tiles that cross a
+// row's causal limit or the live length.
+__device__ __forceinline__ void mask_tile(f32x16& s, int key0, int klim, int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    x[i] = s[i] * c;
-    if (MASK) {
-      const int key = key0 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      x[i] = key < klim ? x[i] : neg_inf();
-    }
-  }
-  float mx = x[0];
+  for (int i = 0; i < 16; ++i) s[i] = key0 + acc_key(i, lane) < klim ? s[i] : neg_inf();
+}
+
+// Growth of the row max (log2 units) tolerated before the accumulator is
+// rescaled: probabilities are exp2(score - m) with m possibly stale by up to
+// this much, i.e. at most 2^8, harmless in fp32 and bf16.  The result is exact
+// for any reference m; the slack only skips most of the per-tile rescales.
+constexpr float kRescaleSlack = 8.0f;
+
+// Online softmax update and PV for one tile of raw scores s (masked entries
+// already -inf).  c = softmax_scale * log2(e) (* k_descale), c > 0.
+template <int D, bool FP8, int VPITCH>
+__device__ __forceinline__ void softmax_pv(SoftmaxState<D>& st, const f32x16& s, float c,
+                                           const uint8_t* vl, int kb, int lane) {
+  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+  mx = fmaxf(mx, s[15]);
   mx = fmaxf(mx, xor32(mx));
-  const float m_new = fmaxf(st.m, mx);
-  // m_new == -inf: nothing visible yet; use 0 as the reference so that
-  // exp2(-inf - 0) = 0 everywhere instead of NaN.
-  const float ref = m_new == neg_inf() ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - ref);
+  const float mxs = mx * c;
+  if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
+    const float m_new = fmaxf(st.m, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
+    st.m = m_new;
+  }
+  // nothing visible yet: reference 0 so that exp2(-inf) = 0 instead of NaN
+  const float nref = st.m == neg_inf() ? 0.f : -st.m;
   float p[16];
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(x[i] - ref);
+    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, nref));
     psum += p[i];
   }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
+  st.l += psum;
   const bf16x8 p0 = pack_bf16x8(p);
   const bf16x8 p1 = pack_bf16x8(p + 8);
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
-    st.o[t] = mfma32(v_operand<FP8, VTPITCH>(vt, kb, t, 0, lane), p0, st.o[t]);
-    st.o[t] = mfma32(v_operand<FP8, VTPITCH>(vt, kb, t, 1, lane), p1, st.o[t]);
+    st.o[t] = mfma32(v_operand<FP8, VPITCH>(vl, kb, t, 0, lane), p0, st.o[t]);
+    st.o[t] = mfma32(v_operand<FP8, VPITCH>(vl, kb, t, 1, lane), p1, st.o[t]);
   }
 }
 
@@ -501,16 +491,14 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
         store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
         if (Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
         __builtin_amdgcn_wave_barrier();
-        const f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        if (key0 + kSub > kfull) mask_tile(s, key0, klim, lane);
         __builtin_amdgcn_wave_barrier();
         if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key0 + kg * NK, chunk, vr);
-        store_vt<NK, FP8, Gm::vt_pitch_sub>(stage, kg * NK, chunk, vr);
+        store_k<NK, Gm::v_pitch>(stage, kg * NK, chunk, vr);
         if (Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
         __builtin_amdgcn_wave_barrier();
-        if (key0 + kSub <= kfull)
-          softmax_pv<D, FP8, Gm::vt_pitch_sub, false>(st, s, c, key0, klim, stage, 0, lane);
-        else
-          softmax_pv<D, FP8, Gm::vt_pitch_sub, true>(st, s, c, key0, klim, stage, 0, lane);
+        softmax_pv<D, FP8, Gm::v_pitch>(st, s, c, stage, 0, lane);
         __builtin_amdgcn_wave_barrier();
       }
     }
@@ -607,8 +595,6 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   SoftmaxState<D> st;
   state_init(st);
 
-  uint8_t* kl = smem;
-  uint8_t* vt = smem + Gm::tile_k_bytes;
   const int unit = threadIdx.x;
   const bool loader = unit < Gm::pre_units;
   const int chunk = unit % Gm::chunks;
@@ -616,6 +602,9 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   u32x4 kr[NK], vr[NK];
   PageWalk w = pw;
   const int chunk_keys = kPcacheEntries << w.shift;
+  // Two LDS tile buffers: tile t is read from buffer t&1 while tile t+1 is
+  // stored into the other one and tile t+2 is in flight in registers, so each
+  // tile costs one workgroup barrier.
   for (int cb = klo; cb < khi; cb += chunk_keys) {
     const int ce = min(khi, cb + chunk_keys);
     __syncthreads();
@@ -625,35 +614,40 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     if (loader) {
       load_unit<NK>(p.k_pool, w, cb + kg * NK, chunk, kr);
       load_unit<NK>(p.v_pool, w, cb + kg * NK, chunk, vr);
+      store_k<NK, Gm::k_pitch>(smem, kg * NK, chunk, kr);
+      store_k<NK, Gm::v_pitch>(smem + Gm::tile_k_bytes, kg * NK, chunk, vr);
+      const int key1 = cb + min(1, ntiles - 1) * kTile;
+      load_unit<NK>(p.k_pool, w, key1 + kg * NK, chunk, kr);
+      load_unit<NK>(p.v_pool, w, key1 + kg * NK, chunk, vr);
     }
+    __syncthreads();
     for (int tix = 0; tix < ntiles; ++tix) {
       const int key0 = cb + tix * kTile;
-      __syncthreads();
-      if (loader) {
-        store_k<NK, Gm::k_pitch>(kl, kg * NK, chunk, kr);
-        store_vt<NK, FP8, Gm::vt_pitch_tile>(vt, kg * NK, chunk, vr);
-      }
-      __syncthreads();
-      if (loader) {
-        // next tile, or (last tile) the current one again: unconditional so the
-        // load counters stay exact across iterations
-        const int key_next = cb + min(tix + 1, ntiles - 1) * kTile;
-        load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
-        load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
-      }
+      const uint8_t* kl = smem + (tix & 1) * Gm::tile_bytes;
+      const uint8_t* vl = kl + Gm::tile_k_bytes;
       if (wave_active) {
 #pragma unroll
         for (int sb = 0; sb < kTile / kSub; ++sb) {
           const int k0 = key0 + sb * kSub;
           if (k0 < wave_kmax) {
-            const f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
-            if (k0 + kSub <= wave_kfull)
-              softmax_pv<D, FP8, Gm::vt_pitch_tile, false>(st, s, c, k0, klim, vt, sb * kSub, lane);
-            else
-              softmax_pv<D, FP8, Gm::vt_pitch_tile, true>(st, s, c, k0, klim, vt, sb * kSub, lane);
+            f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
+            if (k0 + kSub > wave_kfull) mask_tile(s, k0, klim, lane);
+            softmax_pv<D, FP8, Gm::v_pitch>(st, s, c, vl, sb * kSub, lane);
           }
         }
       }
+      if (loader) {
+        // tile tix+1 (already in registers) into the other buffer, then fetch
+        // tile tix+2 -- or, near the end, a tile already in cache: the loads
+        // are unconditional so the compiler's load counters stay exact
+        uint8_t* kn = smem + ((tix + 1) & 1) * Gm::tile_bytes;
+        store_k<NK, Gm::k_pitch>(kn, kg * NK, chunk, kr);
+        store_k<NK, Gm::v_pitch>(kn + Gm::tile_k_bytes, kg * NK, chunk, vr);
+        const int key2 = cb + min(tix + 2, ntiles - 1) * kTile;
+        load_unit<NK>(p.k_pool, w, key2 + kg * NK, chunk, kr);
+        load_unit<NK>(p.v_pool, w, key2 + kg * NK, chunk, vr);
+      }
+      __syncthreads();
     }
   }
   if (wave_active) {
