@@ -62,8 +62,12 @@ constexpr int kDecWaves = 4;              // waves per workgroup, decode launche
 // so its workgroups run one wave per SIMD with the accumulator in AGPRs.
 template <int MODE, int D>
 struct Block {
-  static constexpr int waves = (MODE == kDecode || D == 256) ? kDecWaves : kWaves;
+  static constexpr int waves = kDecWaves;
   static constexpr int threads = waves * kWave;
+  // prefill schedule: 32-row MFMA column tiles per wave (a second tile would
+  // share every K/V operand read, but its accumulator costs the occupancy that
+  // hides LDS and exp latency -- measured slower)
+  static constexpr int nct = 1;
   static constexpr int waves_per_eu = D == 256 ? 1 : 2;
 };
 constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
@@ -159,7 +163,14 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
   return r;
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, kWave); }
+// Value of lane l^32.  v_permlane32_swap exchanges the upper half of its first
+// operand with the lower half of its second; with both operands x, lanes < 32
+// find their partner in the second result and lanes >= 32 in the first.
+__device__ __forceinline__ float xor32(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 // ---------------------------------------------------------------------------
 // K / V staging: a "unit" is NK consecutive keys x one 16-byte chunk of their rows
@@ -191,19 +202,46 @@ __device__ __forceinline__ void fill_pcache(PageWalk& w, int32_t* pcache, int k_
   for (int i = threadIdx.x; i < n; i += blockDim.x) pcache[i] = w.pt_row[w.first_page + i];
 }
 
-// NK consecutive keys from key0, one 16-byte chunk each.  Keys at or past the
-// end of the cached window (never past the live length) are clamped to its
-// last key: they load finite data that the score mask gives probability 0.
+// NK consecutive keys from key0 (a multiple of NK), one 16-byte chunk each,
+// from the K pool and the V pool (same offsets).  NK divides 16 and every page
+// holds a multiple of 16 keys, so an aligned group never crosses a page: one
+// page-id lookup and one 64-bit page base serve the whole group.  Keys at or
+// past the end of the cached window (never past the live length) are clamped
+// to its last key: they load finite data that the score mask gives
+// probability 0.
+template <int NK>
+__device__ __forceinline__ void load_kv_unit(const uint8_t* __restrict__ kpool,
+                                             const uint8_t* __restrict__ vpool, const PageWalk& w,
+                                             int key0, int chunk, u32x4 (&kr)[NK], u32x4 (&vr)[NK]) {
+  static_assert(NK <= 16 && 16 % NK == 0, "a key group must not cross a page");
+  const int kc0 = min(key0, w.kend - 1);
+  const int64_t page_off = (int64_t)w.pcache[(kc0 >> w.shift) - w.first_page] * w.page_bytes +
+                           w.head_off + chunk * 16;
+  const uint8_t* kb = kpool + page_off;
+  const uint8_t* vb = vpool + page_off;
+  const int slot_mask = (1 << w.shift) - 1;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int slot = min(key0 + i, w.kend - 1) & slot_mask;
+    const uint32_t off = (uint32_t)slot * (uint32_t)w.row_stride_b;
+    kr[i] = *reinterpret_cast<const u32x4*>(kb + off);
+    vr[i] = *reinterpret_cast<const u32x4*>(vb + off);
+  }
+}
+
+// Same for one pool only.
 template <int NK>
 __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ pool, const PageWalk& w,
                                           int key0, int chunk, u32x4 (&r)[NK]) {
-  const uint8_t* base = pool + w.head_off + chunk * 16;
+  static_assert(NK <= 16 && 16 % NK == 0, "a key group must not cross a page");
+  const int kc0 = min(key0, w.kend - 1);
+  const uint8_t* base = pool + (int64_t)w.pcache[(kc0 >> w.shift) - w.first_page] * w.page_bytes +
+                        w.head_off + chunk * 16;
+  const int slot_mask = (1 << w.shift) - 1;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
-    const int key = min(key0 + i, w.kend - 1);
-    const int64_t page = w.pcache[(key >> w.shift) - w.first_page];
-    const int slot = key & ((1 << w.shift) - 1);
-    r[i] = *reinterpret_cast<const u32x4*>(base + page * w.page_bytes + (int64_t)slot * w.row_stride_b);
+    const int slot = min(key0 + i, w.kend - 1) & slot_mask;
+    r[i] = *reinterpret_cast<const u32x4*>(base + (uint32_t)slot * (uint32_t)w.row_stride_b);
   }
 }
 
@@ -287,24 +325,27 @@ __device__ __forceinline__ bf16x8 v_operand(const uint8_t* vl, int kb, int t, in
   }
 }
 
-// Scores of one 32-key tile into s (raw q.k, fp32).
-template <int D, bool FP8, int KPITCH, bool QLDS>
-__device__ __forceinline__ f32x16 score_tile(const uint8_t* kl, int kb, const bf16x8* qreg,
-                                             const uint8_t* ql, int qpitch, int lane) {
-  f32x16 s;
+// Scores of NS consecutive 32-key tiles (key rows kb, kb+32, ...): raw q.k in
+// fp32.  The NS accumulation chains are interleaved so that consecutive MFMAs
+// never wait on each other's results.
+template <int D, bool FP8, int KPITCH, bool QLDS, int NS>
+__device__ __forceinline__ void score_tiles(f32x16 (&s)[NS], const uint8_t* kl, int kb,
+                                            const bf16x8* qreg, const uint8_t* ql, int qpitch,
+                                            int lane) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+  for (int n = 0; n < NS; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[n][i] = 0.f;
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) {
-    const bf16x8 a = k_operand<D, FP8, KPITCH>(kl, kb, j, lane);
     bf16x8 bq;
     if constexpr (QLDS)
       bq = as_bf16x8(*reinterpret_cast<const u32x4*>(ql + (lane & 31) * qpitch + (16 * j + (lane >> 5) * 8) * 2));
     else
       bq = qreg[j];
-    s = mfma32(a, bq, s);
+#pragma unroll
+    for (int n = 0; n < NS; ++n) s[n] = mfma32(k_operand<D, FP8, KPITCH>(kl, kb + kSub * n, j, lane), bq, s[n]);
   }
-  return s;
 }
 
 // Mask the scores of one tile: key index of s[i] in this lane, keys >= klim
@@ -321,15 +362,19 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int key0, int klim, int lan
 // for any reference m; the slack only skips most of the per-tile rescales.
 constexpr float kRescaleSlack = 8.0f;
 
-// Online softmax update and PV for one tile of raw scores s (masked entries
-// already -inf).  c = softmax_scale * log2(e) (* k_descale), c > 0.
-template <int D, bool FP8, int VPITCH>
-__device__ __forceinline__ void softmax_pv(SoftmaxState<D>& st, const f32x16& s, float c,
-                                           const uint8_t* vl, int kb, int lane) {
-  float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+// Online softmax update for NS consecutive 32-key tiles of raw scores of one
+// 32-row column tile (masked entries already -inf): updates (m, l), rescales the
+// accumulator when the row max grew by more than the slack, and returns the
+// probabilities as bf16 PV B-operands.  c = softmax_scale * log2(e) (*
+// k_descale), c > 0.
+template <int D, int NS>
+__device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c,
+                                          bf16x8 (&pb)[NS][2]) {
+  float mx = neg_inf();
 #pragma unroll
-  for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
-  mx = fmaxf(mx, s[15]);
+  for (int n = 0; n < NS; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[n][i]), s[n][i + 1]);
   mx = fmaxf(mx, xor32(mx));
   const float mxs = mx * c;
   if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
@@ -344,21 +389,39 @@ __device__ __forceinline__ void softmax_pv(SoftmaxState<D>& st, const f32x16& s,
   }
   // nothing visible yet: reference 0 so that exp2(-inf) = 0 instead of NaN
   const float nref = st.m == neg_inf() ? 0.f : -st.m;
-  float p[16];
   float psum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, nref));
-    psum += p[i];
+  for (int n = 0; n < NS; ++n) {
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[n][i], c, nref));
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = p[i] + p[i + 8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] += q[i + 4];
+    psum += (q[0] + q[2]) + (q[1] + q[3]);
+    pb[n][0] = pack_bf16x8(p);
+    pb[n][1] = pack_bf16x8(p + 8);
   }
   st.l += psum;
-  const bf16x8 p0 = pack_bf16x8(p);
-  const bf16x8 p1 = pack_bf16x8(p + 8);
+}
+
+// O^T += V^T P^T for NS tiles whose V rows start at row kb of the stage, for
+// NCT column tiles at once: each V operand read from LDS feeds NCT MFMAs.
+template <int D, bool FP8, int VPITCH, int NS, int NCT>
+__device__ __forceinline__ void pv_accum(SoftmaxState<D> (&st)[NCT], const bf16x8 (&pb)[NCT][NS][2],
+                                         const uint8_t* vl, int kb, int lane) {
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
-    st.o[t] = mfma32(v_operand<FP8, VPITCH>(vl, kb, t, 0, lane), p0, st.o[t]);
-    st.o[t] = mfma32(v_operand<FP8, VPITCH>(vl, kb, t, 1, lane), p1, st.o[t]);
-  }
+  for (int n = 0; n < NS; ++n)
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 a = v_operand<FP8, VPITCH>(vl, kb + kSub * n, t, h, lane);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) st[ct].o[t] = mfma32(a, pb[ct][n][h], st[ct].o[t]);
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -460,8 +523,8 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   // keys below kfull are visible to every row of the block
   const int kfull = p.causal ? min(khi, rm.pos0 + 1) : khi;
 
-  SoftmaxState<D> st;
-  state_init(st);
+  SoftmaxState<D> st[1];
+  state_init(st[0]);
 
   PageWalk w = pw;
   const int chunk_keys = kPcacheEntries << w.shift;
@@ -491,14 +554,17 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
         store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
         if (Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
         __builtin_amdgcn_wave_barrier();
-        f32x16 s = score_tile<D, FP8, Gm::k_pitch, true>(stage, 0, nullptr, ql, Gm::q_pitch, lane);
-        if (key0 + kSub > kfull) mask_tile(s, key0, klim, lane);
+        f32x16 s[1];
+        score_tiles<D, FP8, Gm::k_pitch, true, 1>(s, stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        if (key0 + kSub > kfull) mask_tile(s[0], key0, klim, lane);
         __builtin_amdgcn_wave_barrier();
         if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key0 + kg * NK, chunk, vr);
         store_k<NK, Gm::v_pitch>(stage, kg * NK, chunk, vr);
         if (Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
         __builtin_amdgcn_wave_barrier();
-        softmax_pv<D, FP8, Gm::v_pitch>(st, s, c, stage, 0, lane);
+        bf16x8 pb[1][1][2];
+        softmax_p<D, 1>(st[0], s, c, pb[0]);
+        pv_accum<D, FP8, Gm::v_pitch, 1, 1>(st, pb, stage, 0, lane);
         __builtin_amdgcn_wave_barrier();
       }
     }
@@ -523,32 +589,32 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) buf[(t * 16 + i) * kWave + lane] = st.o[t][i];
-      buf[(D / 2) * kWave + lane] = st.l;
-      buf[(D / 2 + 1) * kWave + lane] = st.m;
+        for (int i = 0; i < 16; ++i) buf[(t * 16 + i) * kWave + lane] = st[0].o[t][i];
+      buf[(D / 2) * kWave + lane] = st[0].l;
+      buf[(D / 2 + 1) * kWave + lane] = st[0].m;
     }
     __syncthreads();
     if (wave >= r_lo && wave < w_lo) {
       const float* buf = red + (wave - r_lo) * Gm::red_floats * kWave;
       const float l2 = buf[(D / 2) * kWave + lane];
       const float m2 = buf[(D / 2 + 1) * kWave + lane];
-      const float mm = fmaxf(st.m, m2);
+      const float mm = fmaxf(st[0].m, m2);
       const float ref = mm == neg_inf() ? 0.f : mm;
-      const float a1 = __builtin_amdgcn_exp2f(st.m - ref);
+      const float a1 = __builtin_amdgcn_exp2f(st[0].m - ref);
       const float a2 = __builtin_amdgcn_exp2f(m2 - ref);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st.o[t][i] = st.o[t][i] * a1 + buf[(t * 16 + i) * kWave + lane] * a2;
-      st.l = st.l * a1 + l2 * a2;
-      st.m = mm;
+        for (int i = 0; i < 16; ++i) st[0].o[t][i] = st[0].o[t][i] * a1 + buf[(t * 16 + i) * kWave + lane] * a2;
+      st[0].l = st[0].l * a1 + l2 * a2;
+      st[0].m = mm;
     }
     __syncthreads();
     active = w_lo;
   }
   if (wave == 0) {
-    const float l_tot = st.l + xor32(st.l);
-    write_rows<D>(p, st, l_tot, 0, rm, split, vdesc, lane);
+    const float l_tot = st[0].l + xor32(st[0].l);
+    write_rows<D>(p, st[0], l_tot, 0, rm, split, vdesc, lane);
   }
 }
 
@@ -556,44 +622,54 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 // prefill schedule: each wave owns 32 packed query rows; K/V tiles shared in LDS
 // ---------------------------------------------------------------------------
 
-template <int D, bool FP8>
+template <int D, bool FP8, int MODE>
 __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
   constexpr int NK = Gm::pre_keys_per_unit;
+  constexpr int NCT = Block<MODE, D>::nct;               // 32-row column tiles per wave
+  constexpr int NS = kTile / kSub;                       // score tiles per LDS tile
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrows = rm.ntok * rm.G;
-  const int r0 = wave * kCols;               // this wave's first packed row
+  const int r0 = wave * kCols * NCT;                     // this wave's first packed row
+  const int last_tok = max(rm.ntok - 1, 0);
 
-  // Q operand for this wave's rows, in registers
-  bf16x8 qreg[D / 16];
-  {
-    const int r = r0 + (lane & 31);
+  // Q operands of this wave's rows, in registers
+  bf16x8 qreg[NCT][D / 16];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int r = r0 + ct * kCols + (lane & 31);
     const bool ok = r < nrows;
     const int tok = ok ? r / rm.G : 0;
     const int h = rm.g * rm.G + (r - tok * rm.G);
     const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
 #pragma unroll
     for (int j = 0; j < D / 16; ++j)
-      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j))
-                   : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      qreg[ct][j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j))
+                       : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
   const int klo = split * p.split_keys;
   int khi = min(L, klo + p.split_keys);
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
-  // wave-level visibility: rows of this wave are tokens [tok_a, tok_b]
+
+  // visibility: the wave's rows are tokens [tok_a, tok_b]; lane rows per column tile
   const bool wave_active = r0 < nrows;
-  const int tok_a = min(r0 / rm.G, max(rm.ntok - 1, 0));
-  const int tok_b = min((r0 + kCols - 1) / rm.G, max(rm.ntok - 1, 0));
+  const int tok_a = min(r0 / rm.G, last_tok);
+  const int tok_b = min((r0 + kCols * NCT - 1) / rm.G, last_tok);
   const int wave_kmax = p.causal ? min(khi, rm.pos0 + tok_b + 1) : khi;   // no key >= this is visible
   const int wave_kfull = p.causal ? min(khi, rm.pos0 + tok_a + 1) : khi;  // keys < this visible to all
-  const int my_tok = min((r0 + (lane & 31)) / rm.G, max(rm.ntok - 1, 0));
-  const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
+  int klim[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int my_tok = min((r0 + ct * kCols + (lane & 31)) / rm.G, last_tok);
+    klim[ct] = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
+  }
 
-  SoftmaxState<D> st;
-  state_init(st);
+  SoftmaxState<D> st[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) state_init(st[ct]);
 
   const int unit = threadIdx.x;
   const bool loader = unit < Gm::pre_units;
@@ -612,28 +688,41 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     __syncthreads();
     const int ntiles = (ce - cb + kTile - 1) / kTile;
     if (loader) {
-      load_unit<NK>(p.k_pool, w, cb + kg * NK, chunk, kr);
-      load_unit<NK>(p.v_pool, w, cb + kg * NK, chunk, vr);
+      load_kv_unit<NK>(p.k_pool, p.v_pool, w, cb + kg * NK, chunk, kr, vr);
       store_k<NK, Gm::k_pitch>(smem, kg * NK, chunk, kr);
       store_k<NK, Gm::v_pitch>(smem + Gm::tile_k_bytes, kg * NK, chunk, vr);
       const int key1 = cb + min(1, ntiles - 1) * kTile;
-      load_unit<NK>(p.k_pool, w, key1 + kg * NK, chunk, kr);
-      load_unit<NK>(p.v_pool, w, key1 + kg * NK, chunk, vr);
+      load_kv_unit<NK>(p.k_pool, p.v_pool, w, key1 + kg * NK, chunk, kr, vr);
     }
     __syncthreads();
     for (int tix = 0; tix < ntiles; ++tix) {
       const int key0 = cb + tix * kTile;
       const uint8_t* kl = smem + (tix & 1) * Gm::tile_bytes;
       const uint8_t* vl = kl + Gm::tile_k_bytes;
-      if (wave_active) {
+      if (wave_active && key0 < wave_kmax) {
 #pragma unroll
-        for (int sb = 0; sb < kTile / kSub; ++sb) {
-          const int k0 = key0 + sb * kSub;
-          if (k0 < wave_kmax) {
-            f32x16 s = score_tile<D, FP8, Gm::k_pitch, false>(kl, sb * kSub, qreg, nullptr, 0, lane);
-            if (k0 + kSub > wave_kfull) mask_tile(s, k0, klim, lane);
-            softmax_pv<D, FP8, Gm::v_pitch>(st, s, c, vl, sb * kSub, lane);
+        for (int n = 0; n < NS; ++n) {
+          const int k0 = key0 + kSub * n;
+          // S^T of one 32-key tile for NCT column tiles; each K operand feeds NCT MFMAs
+          f32x16 s[NCT][1];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[ct][0][i] = 0.f;
+#pragma unroll
+          for (int j = 0; j < D / 16; ++j) {
+            const bf16x8 a = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j, lane);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) s[ct][0] = mfma32(a, qreg[ct][j], s[ct][0]);
           }
+          if (k0 + kSub > wave_kfull) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) mask_tile(s[ct][0], k0, klim[ct], lane);
+          }
+          bf16x8 pb[NCT][1][2];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) softmax_p<D, 1>(st[ct], s[ct], c, pb[ct]);
+          pv_accum<D, FP8, Gm::v_pitch, 1, NCT>(st, pb, vl, kSub * n, lane);
         }
       }
       if (loader) {
@@ -644,15 +733,17 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
         store_k<NK, Gm::k_pitch>(kn, kg * NK, chunk, kr);
         store_k<NK, Gm::v_pitch>(kn + Gm::tile_k_bytes, kg * NK, chunk, vr);
         const int key2 = cb + min(tix + 2, ntiles - 1) * kTile;
-        load_unit<NK>(p.k_pool, w, key2 + kg * NK, chunk, kr);
-        load_unit<NK>(p.v_pool, w, key2 + kg * NK, chunk, vr);
+        load_kv_unit<NK>(p.k_pool, p.v_pool, w, key2 + kg * NK, chunk, kr, vr);
       }
       __syncthreads();
     }
   }
   if (wave_active) {
-    const float l_tot = st.l + xor32(st.l);
-    write_rows<D>(p, st, l_tot, r0, rm, split, vdesc, lane);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float l_tot = st[ct].l + xor32(st[ct].l);
+      write_rows<D>(p, st[ct], l_tot, r0 + ct * kCols, rm, split, vdesc, lane);
+    }
   }
 }
 
@@ -731,12 +822,12 @@ void attn_kernel(AttnParams p) {
   if constexpr (MODE == kDecode) {
     keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
-    rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
+    rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
     if (q_len * p.group <= kCols)
       keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
     else
-      rowsplit_item<D, FP8>(p, smem, pcache, rm, pw, L, split, c, vdesc);
+      rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   }
 }
 
@@ -833,9 +924,9 @@ int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
 
 int prefill_block_rows(int head_dim) {
   switch (head_dim) {
-    case 64: return Block<kPrefill, 64>::waves * kCols;
-    case 128: return Block<kPrefill, 128>::waves * kCols;
-    case 256: return Block<kPrefill, 256>::waves * kCols;
+    case 64: return Block<kPrefill, 64>::waves * Block<kPrefill, 64>::nct * kCols;
+    case 128: return Block<kPrefill, 128>::waves * Block<kPrefill, 128>::nct * kCols;
+    case 256: return Block<kPrefill, 256>::waves * Block<kPrefill, 256>::nct * kCols;
   }
   return 0;
 }
