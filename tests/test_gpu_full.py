@@ -1,0 +1,67 @@
+"""GPU parity at full size: the four large workloads in the launch configuration
+bench.py times (plus the other entry points that accept them), compared with
+the oracle on sampled rows -- every sequence's first and last query token and
+random ones, each with several query heads."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_gqa_attention_amd import synth
+from paged_kv_gqa_attention_amd.attention import DeviceInputs, PagedAttention
+from tests import helpers as H
+from tests.test_gpu_parity import check
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def run_sampled(w, mode, num_splits=0, per_seq=3, heads=4):
+    print("case", w.name, mode, "splits", num_splits, flush=True)
+    x = DeviceInputs(w)
+    pa = PagedAttention(w, num_splits=num_splits)
+    out, lse = pa.run(mode, x)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(w, per_seq=per_seq, heads=heads)
+    ref = H.run_oracle(w, rows=rows)
+    return check(w, out, lse, ref[0], ref[1], rows=rows,
+                 what="%s/%s/S%d" % (w.name, mode, pa.info.num_splits))
+
+
+def test_decode_llama8b_full():
+    w = synth.decode_llama8b()
+    run_sampled(w, "decode")
+    run_sampled(w, "decode", num_splits=3)
+    run_sampled(w, "mixed")
+
+
+def test_prefill_causal_full():
+    w = synth.prefill_causal()
+    run_sampled(w, "prefill", per_seq=6)
+    run_sampled(w, "mixed", per_seq=6)
+
+
+def test_mixed_24b_full():
+    w = synth.mixed_24b()
+    run_sampled(w, "mixed", per_seq=4)
+    run_sampled(w, "prefill", per_seq=4)
+    ws = synth.mixed_24b(shuffle=True)
+    run_sampled(ws, "mixed", per_seq=4)
+
+
+def test_decode_fp8_long_full():
+    w = synth.decode_fp8_long()
+    run_sampled(w, "decode", heads=8)
+    run_sampled(w, "decode", num_splits=1, heads=8)
+    run_sampled(w, "mixed", heads=8)
+
+
+def test_full_size_outputs_are_finite_everywhere():
+    # every row, not just the sample: poisoned tails never leak
+    for make, mode in ((synth.decode_llama8b, "decode"), (synth.decode_fp8_long, "decode"),
+                       (synth.mixed_24b, "mixed")):
+        w = make()
+        x = DeviceInputs(w)
+        pa = PagedAttention(w)
+        out, lse = pa.run(mode, x)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out.float()).all()), w.name
+        assert bool(torch.isfinite(lse).all()), w.name

@@ -1,0 +1,158 @@
+"""libpa.so without a GPU: every declared symbol is exported, plans validate
+geometry and fail closed, workspace sizes follow the split choice, and runs
+reject bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_gqa_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def desc(**kw):
+    d = dict(num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+             num_pages=100, page_table_cols=16, max_total_q=4, max_q_len=1, max_seq_len=256,
+             kv_dtype=B.PA_KV_BF16, num_splits=0, num_cus=256)
+    d.update(kw)
+    return B.make_desc(**d)
+
+
+def plan_status(**kw):
+    try:
+        p = B.pa_plan(desc(**kw))
+    except B.PaError as e:
+        return e.code
+    B.pa_plan_destroy(p)
+    return B.PA_OK
+
+
+def test_status_strings():
+    for code in (B.PA_OK, B.PA_ERR_INVALID, B.PA_ERR_UNSUPPORTED, B.PA_ERR_WORKSPACE, B.PA_ERR_HIP):
+        assert B.pa_status_str(code).startswith("PA_")
+    assert "unknown" in B.pa_status_str(-99)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, B.PA_OK),
+    (dict(head_dim=96), B.PA_ERR_UNSUPPORTED),
+    (dict(head_dim=512), B.PA_ERR_UNSUPPORTED),
+    (dict(page_size=8), B.PA_ERR_UNSUPPORTED),
+    (dict(page_size=256), B.PA_ERR_UNSUPPORTED),
+    (dict(page_size=48), B.PA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=24, num_kv_heads=8), B.PA_ERR_UNSUPPORTED),     # G = 3
+    (dict(num_q_heads=64, num_kv_heads=1), B.PA_ERR_UNSUPPORTED),     # G = 64 > 32
+    (dict(num_q_heads=30, num_kv_heads=8), B.PA_ERR_INVALID),         # Hq % Hkv
+    (dict(num_kv_heads=0), B.PA_ERR_INVALID),
+    (dict(num_seqs=-1), B.PA_ERR_INVALID),
+    (dict(page_table_cols=8, page_table_row_stride=4), B.PA_ERR_INVALID),
+    (dict(kv_dtype=7), B.PA_ERR_INVALID),
+    (dict(max_seq_len=10_000), B.PA_ERR_INVALID),                    # > C * page
+    (dict(kv_page_stride=100), B.PA_ERR_INVALID),                     # < dense page
+    (dict(num_splits=-2), B.PA_ERR_INVALID),
+    (dict(num_q_heads=64, num_kv_heads=2, head_dim=256, page_size=128, kv_dtype=B.PA_KV_FP8_E4M3), B.PA_OK),
+    (dict(num_q_heads=4, num_kv_heads=4, head_dim=64), B.PA_OK),       # MHA
+    (dict(num_seqs=0, max_total_q=0), B.PA_OK),                        # empty batch
+])
+def test_plan_validation(kw, code):
+    assert plan_status(**kw) == code
+
+
+def test_plan_null_arguments():
+    h = ctypes.c_void_p()
+    assert B.lib().pa_plan(None, ctypes.byref(h)) == B.PA_ERR_INVALID
+    d = desc()
+    assert B.lib().pa_plan(ctypes.byref(d), None) == B.PA_ERR_INVALID
+    assert B.pa_workspace_bytes(None) == 0
+    B.pa_plan_destroy(None)
+
+
+def test_split_heuristic_and_workspace():
+    # few (sequence, head) items and long contexts: split; workspace holds partials
+    p = B.pa_plan(desc(num_seqs=64, num_q_heads=64, num_kv_heads=2, head_dim=256, page_size=128,
+                       page_table_cols=256, max_total_q=64, max_seq_len=32768,
+                       kv_dtype=B.PA_KV_FP8_E4M3))
+    info = B.pa_plan_get_info(p)
+    S = info.num_splits
+    assert S > 1 and info.split_keys % 128 == 0 and S * info.split_keys >= 256 * 128
+    rows = S * 64 * 64
+    assert B.pa_workspace_bytes(p) >= rows * 256 * 4 + rows * 4
+    assert info.workspace_bytes == B.pa_workspace_bytes(p)
+    B.pa_plan_destroy(p)
+    # many items: no split, no workspace
+    p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048))
+    assert B.pa_plan_get_info(p).num_splits == 1 and B.pa_workspace_bytes(p) == 0
+    B.pa_plan_destroy(p)
+    # forced splits are honoured (rounded to whole 128-key windows)
+    p = B.pa_plan(desc(num_splits=3, page_table_cols=64, max_seq_len=1024))
+    info = B.pa_plan_get_info(p)
+    assert info.num_splits == 3 and info.split_keys == 384
+    B.pa_plan_destroy(p)
+
+
+def test_prefill_block_shape():
+    for D, G in ((64, 2), (128, 4), (256, 32)):
+        p = B.pa_plan(desc(head_dim=D, num_q_heads=8 * G, num_kv_heads=8))
+        info = B.pa_plan_get_info(p)
+        assert info.group == G and info.q_block_tokens >= 1
+        B.pa_plan_destroy(p)
+
+
+def test_runs_reject_bad_arguments_without_touching_the_device():
+    p = B.pa_plan(desc())
+    a = B.pa_args()                       # all pointers NULL
+    a.softmax_scale = 0.1
+    for fn in (B.lib().pa_run_decode, B.lib().pa_run_prefill, B.lib().pa_run_mixed):
+        assert fn(p, ctypes.byref(a), None) == B.PA_ERR_INVALID
+    assert B.lib().pa_run_decode(p, None, None) == B.PA_ERR_INVALID
+    assert B.lib().pa_run_decode(None, ctypes.byref(a), None) == B.PA_ERR_INVALID
+    # misaligned pointers, bad scale, bad strides: fake non-null addresses are
+    # never dereferenced because validation fails first
+    good = dict(q=4096, k_pool=8192, v_pool=12288, page_table=16384, cu_q_lens=20480,
+                seq_lens=24576, out=28672)
+    def args(**kw):
+        v = dict(good)
+        v.update(kw)
+        x = B.pa_args(**{k: v[k] for k in good})
+        x.softmax_scale = kw.get("scale", 0.1)
+        x.q_stride_t = kw.get("q_stride_t", 0)
+        x.o_stride_t = kw.get("o_stride_t", 0)
+        return x
+    for bad in (args(q=4100), args(out=28674), args(scale=0.0), args(scale=-1.0),
+                args(scale=float("nan")), args(q_stride_t=4000), args(o_stride_t=4100)):
+        assert B.lib().pa_run_decode(p, ctypes.byref(bad), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
+    # fp8 without descales
+    p = B.pa_plan(desc(kv_dtype=B.PA_KV_FP8_E4M3))
+    x = args()
+    assert B.lib().pa_run_decode(p, ctypes.byref(x), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
+    # a split plan without workspace
+    p = B.pa_plan(desc(num_splits=4, page_table_cols=64, max_seq_len=1024))
+    x = args()
+    assert B.lib().pa_run_decode(p, ctypes.byref(x), None) == B.PA_ERR_WORKSPACE
+    x.workspace = 1 << 20
+    x.workspace_bytes = 16
+    assert B.lib().pa_run_decode(p, ctypes.byref(x), None) == B.PA_ERR_WORKSPACE
+    # prefill needs no workspace but needs cu_q_lens
+    y = args(cu_q_lens=None)
+    y.cu_q_lens = None
+    assert B.lib().pa_run_prefill(p, ctypes.byref(y), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
