@@ -75,6 +75,7 @@ constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
 constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
 constexpr int kLdsMax = 160 * 1024;
 constexpr int kPcacheEntries = 1024;      // page ids cached in LDS per chunk of keys
+constexpr int kXcds = 8;                  // accelerator complex dies of an MI355X
 constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
@@ -703,18 +704,34 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const int k0 = key0 + kSub * n;
-          // S^T of one 32-key tile for NCT column tiles; each K operand feeds NCT MFMAs
-          f32x16 s[NCT][1];
+          // all K operands of the tile first, so the score MFMAs do not wait
+          // on LDS one by one
+          bf16x8 ka[D / 16];
+#pragma unroll
+          for (int j = 0; j < D / 16; ++j) ka[j] = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j, lane);
+          // two independent accumulation chains (even / odd k-steps) halve the
+          // dependent-MFMA latency of the score product
+          f32x16 s[NCT][1], s2[NCT];
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[ct][0][i] = 0.f;
+            for (int i = 0; i < 16; ++i) s[ct][0][i] = s2[ct][i] = 0.f;
 #pragma unroll
-          for (int j = 0; j < D / 16; ++j) {
-            const bf16x8 a = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j, lane);
+          for (int j = 0; j < D / 16; j += 2)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) s[ct][0] = mfma32(a, qreg[ct][j], s[ct][0]);
-          }
+            for (int ct = 0; ct < NCT; ++ct) {
+              s[ct][0] = mfma32(ka[j], qreg[ct][j], s[ct][0]);
+              s2[ct] = mfma32(ka[j + 1], qreg[ct][j + 1], s2[ct]);
+            }
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) s[ct][0] += s2[ct];
+          // V operands requested before the softmax: their LDS latency hides
+          // under the exp work
+          bf16x8 va[D / 32][2];
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) va[t][h] = v_operand<FP8, Gm::v_pitch>(vl, kSub * n, t, h, lane);
           if (k0 + kSub > wave_kfull) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) mask_tile(s[ct][0], k0, klim[ct], lane);
@@ -722,7 +739,12 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
           bf16x8 pb[NCT][1][2];
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) softmax_p<D, 1>(st[ct], s[ct], c, pb[ct]);
-          pv_accum<D, FP8, Gm::v_pitch, 1, NCT>(st, pb, vl, kSub * n, lane);
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) st[ct].o[t] = mfma32(va[t][h], pb[ct][0][h], st[ct].o[t]);
         }
       }
       if (loader) {
@@ -758,8 +780,8 @@ void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
-  const int g = blockIdx.y;
   const int split = blockIdx.z;
+  int g = blockIdx.y;
   int b, t0, ntok, q_len, i0 = 0;
   if constexpr (MODE == kDecode) {
     b = blockIdx.x;
@@ -777,7 +799,21 @@ void attn_kernel(AttnParams p) {
     // [cu[b]/BQ + b, cu[b]/BQ + b + ceil(q_len_b/BQ)), which never overlap
     // and stay below cu[B]/BQ + B, so the grid can be sized from host bounds.
     const int BQ = p.q_block_tokens;
-    const int x = blockIdx.x;
+    // Workgroups are dealt to the XCDs round-robin by linear id.  Remap so that
+    // each XCD takes a contiguous range of the logical list (KV head major,
+    // then q-block): the q-blocks that stream the same K/V share one L2.
+    // Within a sequence the q-blocks run last-first, the ones with the most
+    // keys first.
+    int x;
+    {
+      const int X = gridDim.x;
+      const int n = X * gridDim.y;
+      const int lin = blockIdx.x + X * blockIdx.y;
+      const int full = n - n % kXcds;
+      const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
+      g = logical / X;
+      x = X - 1 - (logical - g * X);
+    }
     if (threadIdx.x == 0) meta[0] = 0;
     __syncthreads();
     int cnt = 0;
