@@ -96,9 +96,13 @@ struct Geo {
   // (ds_read_b64_tr_b16 / _tr_b8); the extra pad staggers the rows one
   // transposed read touches across banks.
   static constexpr int v_pitch = row_bytes + 32;
-  // decode schedule: per-wave 32-key stage; K rows, then V rows, in one region
-  static constexpr int dec_keys_per_lane = (kSub * chunks) / kWave;   // >= 1
-  static constexpr int stage_bytes = CMax<kSub * k_pitch, kSub * v_pitch>::value;
+  // decode schedule: each wave step stages dec_step keys (K rows, then V rows,
+  // in one region).  fp8 at head dim 256 runs one wave per SIMD and has the
+  // registers to keep two 32-key tiles (32 KB) in flight per wave.
+  static constexpr int dec_tiles = (D == 256 && FP8) ? 2 : 1;
+  static constexpr int dec_step = kSub * dec_tiles;
+  static constexpr int dec_keys_per_lane = (dec_step * chunks) / kWave;   // >= 1
+  static constexpr int stage_bytes = CMax<dec_step * k_pitch, dec_step * v_pitch>::value;
   static constexpr int q_bytes = kCols * q_pitch;
   // waves of a decode-schedule item that stage K/V (for an NWB-wave workgroup)
   template <int NWB>
@@ -534,7 +538,9 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     __syncthreads();
     fill_pcache(w, pcache, cb, ce);
     __syncthreads();
-    const int nsub = (ce - cb + kSub - 1) / kSub;
+    constexpr int STEP = Gm::dec_step;
+    constexpr int NT = Gm::dec_tiles;
+    const int nsub = (ce - cb + STEP - 1) / STEP;
     if (wave < NW) {
       uint8_t* stage = smem + Gm::q_bytes + wave * Gm::stage_bytes;
       const int chunk = lane % Gm::chunks;
@@ -542,30 +548,33 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
       u32x4 kr[NK], vr[NK];
       int n = wave;
       if (Gm::dec_prefetch && n < nsub) {
-        load_unit<NK>(p.k_pool, w, cb + n * kSub + kg * NK, chunk, kr);
-        load_unit<NK>(p.v_pool, w, cb + n * kSub + kg * NK, chunk, vr);
+        load_unit<NK>(p.k_pool, w, cb + n * STEP + kg * NK, chunk, kr);
+        load_unit<NK>(p.v_pool, w, cb + n * STEP + kg * NK, chunk, vr);
       }
       for (; n < nsub; n += NW) {
-        const int key0 = cb + n * kSub;
-        // Prefetch target: the wave's next sub-tile, or (last iteration) a
-        // sub-tile already in cache.  Unconditional, so that the compiler's
-        // load counters stay exact and no wait covers the prefetch itself.
-        const int key_next = cb + min(n + NW, nsub - 1) * kSub;
+        const int key0 = cb + n * STEP;
+        // Prefetch target: the wave's next step, or (last iteration) keys
+        // already in cache.  Unconditional, so that the compiler's load
+        // counters stay exact and no wait covers the prefetch itself.
+        const int key_next = cb + min(n + NW, nsub - 1) * STEP;
         if (!Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key0 + kg * NK, chunk, kr);
         store_k<NK, Gm::k_pitch>(stage, kg * NK, chunk, kr);
         if (Gm::dec_prefetch) load_unit<NK>(p.k_pool, w, key_next + kg * NK, chunk, kr);
         __builtin_amdgcn_wave_barrier();
-        f32x16 s[1];
-        score_tiles<D, FP8, Gm::k_pitch, true, 1>(s, stage, 0, nullptr, ql, Gm::q_pitch, lane);
-        if (key0 + kSub > kfull) mask_tile(s[0], key0, klim, lane);
+        f32x16 s[NT];
+        score_tiles<D, FP8, Gm::k_pitch, true, NT>(s, stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        if (key0 + STEP > kfull) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) mask_tile(s[t], key0 + kSub * t, klim, lane);
+        }
         __builtin_amdgcn_wave_barrier();
         if (!Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key0 + kg * NK, chunk, vr);
         store_k<NK, Gm::v_pitch>(stage, kg * NK, chunk, vr);
         if (Gm::dec_prefetch) load_unit<NK>(p.v_pool, w, key_next + kg * NK, chunk, vr);
         __builtin_amdgcn_wave_barrier();
-        bf16x8 pb[1][1][2];
-        softmax_p<D, 1>(st[0], s, c, pb[0]);
-        pv_accum<D, FP8, Gm::v_pitch, 1, 1>(st, pb, stage, 0, lane);
+        bf16x8 pb[1][NT][2];
+        softmax_p<D, NT>(st[0], s, c, pb[0]);
+        pv_accum<D, FP8, Gm::v_pitch, NT, 1>(st, pb, stage, 0, lane);
         __builtin_amdgcn_wave_barrier();
       }
     }
@@ -802,8 +811,8 @@ void attn_kernel(AttnParams p) {
     // Workgroups are dealt to the XCDs round-robin by linear id.  Remap so that
     // each XCD takes a contiguous range of the logical list (KV head major,
     // then q-block): the q-blocks that stream the same K/V share one L2.
-    // Within a sequence the q-blocks run last-first, the ones with the most
-    // keys first.
+    // Prefill runs each sequence's q-blocks last-first (most keys first);
+    // mixed batches keep the caller's sequence order.
     int x;
     {
       const int X = gridDim.x;
@@ -812,7 +821,8 @@ void attn_kernel(AttnParams p) {
       const int full = n - n % kXcds;
       const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
       g = logical / X;
-      x = X - 1 - (logical - g * X);
+      x = logical - g * X;
+      if (MODE == kPrefill) x = X - 1 - x;
     }
     if (threadIdx.x == 0) meta[0] = 0;
     __syncthreads();
