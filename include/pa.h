@@ -169,10 +169,10 @@ typedef struct {
 typedef struct {
   int32_t num_splits;        /* split-KV factor used by decode and mixed runs */
   int32_t split_keys;        /* keys per split window (multiple of the key tile) */
-  int32_t q_block_tokens;    /* query tokens per work item of prefill/mixed runs */
+  int32_t q_block_tokens;    /* query tokens per work item of prefill runs */
   int32_t group;             /* G = Hq / Hkv */
   int32_t num_cus;           /* compute units planned for */
-  int32_t reserved;
+  int32_t mixed_q_block_tokens;  /* query tokens per work item of mixed runs */
   size_t workspace_bytes;    /* = pa_workspace_bytes(plan) */
 } pa_plan_info;
 

@@ -92,7 +92,7 @@ class pa_plan_info(ctypes.Structure):
         ("q_block_tokens", ctypes.c_int32),
         ("group", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("mixed_q_block_tokens", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

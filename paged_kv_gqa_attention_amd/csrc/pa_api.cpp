@@ -35,7 +35,8 @@ struct pa_plan_s {
   int32_t esz;
   int32_t num_splits;
   int32_t split_keys;
-  int32_t q_block_tokens;
+  int32_t q_block_tokens;          // prefill launches
+  int32_t mixed_q_block_tokens;    // mixed launches
   int32_t num_cus;
   int32_t rows_cap;          // token rows the partial buffers are laid out for
   int64_t kv_page_bytes;
@@ -97,7 +98,8 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   p->page_shift = ilog2(d.page_size);
   p->esz = esz;
   p->num_cus = cus;
-  p->q_block_tokens = std::max(1, pa::prefill_block_rows(d.head_dim) / G);
+  p->q_block_tokens = std::max(1, pa::block_rows(d.head_dim, pa::kPrefill) / G);
+  p->mixed_q_block_tokens = std::max(1, pa::block_rows(d.head_dim, pa::kMixed) / G);
   p->kv_page_bytes = page_elems * esz;
   p->rows_cap = std::max(d.max_total_q, d.num_seqs);
 
@@ -107,7 +109,7 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   const int64_t max_len = d.max_seq_len ? d.max_seq_len : capacity;
   int splits = d.num_splits;
   if (splits == 0) {
-    const int64_t qblocks = std::max<int64_t>(1, ceil_div(d.max_total_q, p->q_block_tokens));
+    const int64_t qblocks = std::max<int64_t>(1, ceil_div(d.max_total_q, p->mixed_q_block_tokens));
     const int64_t items = std::max<int64_t>(1, std::max<int64_t>(d.num_seqs, qblocks)) * d.num_kv_heads;
     const int64_t want = ceil_div(4 * (int64_t)cus, items);
     const int64_t by_len = std::max<int64_t>(1, max_len / kMinSplitKeys);
@@ -138,6 +140,7 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info) {
   info->num_splits = plan->num_splits;
   info->split_keys = plan->split_keys;
   info->q_block_tokens = plan->q_block_tokens;
+  info->mixed_q_block_tokens = plan->mixed_q_block_tokens;
   info->group = plan->group;
   info->num_cus = plan->num_cus;
   info->workspace_bytes = plan->ws_bytes;
@@ -210,7 +213,7 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   p.part_o = part_o;
   p.part_lse = part_lse;
   p.max_total_q = plan->rows_cap;
-  p.q_block_tokens = plan->q_block_tokens;
+  p.q_block_tokens = mode == pa::kPrefill ? plan->q_block_tokens : plan->mixed_q_block_tokens;
   return PA_OK;
 }
 
@@ -221,7 +224,7 @@ pa_status launch(pa_plan_t plan, const pa::AttnParams& p, pa::Mode mode, hipStre
   if (mode == pa::kDecode) {
     grid = dim3((unsigned)d.num_seqs, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
   } else {
-    const int64_t blocks = (int64_t)plan->rows_cap / plan->q_block_tokens + d.num_seqs;
+    const int64_t blocks = (int64_t)plan->rows_cap / p.q_block_tokens + d.num_seqs;
     grid = dim3((unsigned)blocks, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
   }
   const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;

@@ -69,8 +69,8 @@ hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnPara
 hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream);
 // LDS bytes the attention instance uses (host-side check).
 int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode);
-// Packed query rows (tokens x GQA heads) per prefill/mixed workgroup.
-int prefill_block_rows(int head_dim);
+// Packed query rows (tokens x GQA heads) per workgroup of a launch mode.
+int block_rows(int head_dim, Mode mode);
 
 }  // namespace pa
 

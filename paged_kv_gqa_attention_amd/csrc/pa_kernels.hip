@@ -52,17 +52,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;                 // waves per workgroup, prefill and mixed launches
-constexpr int kThreads = kWave * kWaves;
-constexpr int kDecWaves = 4;              // waves per workgroup, decode launches
+constexpr int kDecWaves = 4;              // waves per workgroup, decode and mixed launches
+constexpr int kStreamWaves = 8;           // waves per workgroup, streamed prefill
 
-// Workgroup shape of a launch.  Decode workgroups are half size so that two
-// of them share a compute unit and one's prologue/epilogue overlaps the
-// other's streaming.  Head dim 256 keeps a 128-row fp32 accumulator per wave,
-// so its workgroups run one wave per SIMD with the accumulator in AGPRs.
+// Workgroup shape of a launch.  Decode and mixed workgroups have 4 waves so
+// that two of them share a compute unit and one's prologue/epilogue overlaps
+// the other's streaming.  Prefill at head dim <= 128 runs the streamed
+// schedule: 8 waves (two per SIMD), one workgroup per compute unit, all of
+// LDS a ring of K/V tiles.  Head dim 256 keeps a 128-row fp32 accumulator per
+// wave, so its workgroups run one wave per SIMD with the accumulator in AGPRs.
 template <int MODE, int D>
 struct Block {
-  static constexpr int waves = kDecWaves;
+  static constexpr bool stream = MODE == kPrefill && D <= 128;
+  static constexpr int waves = stream ? kStreamWaves : kDecWaves;
   static constexpr int threads = waves * kWave;
   // prefill schedule: 32-row MFMA column tiles per wave (a second tile would
   // share every K/V operand read, but its accumulator costs the occupancy that
@@ -108,12 +110,17 @@ struct Geo {
   template <int NWB>
   struct DecWaves { static constexpr int value = (NWB * stage_bytes + q_bytes <= kLdsMax - 8192) ? NWB : NWB / 2; };
   static constexpr bool dec_prefetch = chunks <= 16;   // keep staging registers <= 64 VGPRs
-  // prefill schedule: 64-key tile, K and V^T resident together
-  static constexpr int pre_threads = Block<kPrefill, D>::threads;
-  static constexpr int pre_keys_per_unit = (kTile * chunks) / pre_threads > 0 ? (kTile * chunks) / pre_threads : 1;
-  static constexpr int pre_units = (kTile * chunks) / pre_keys_per_unit;
+  // prefill schedules: 64-key tile, K rows then V rows at their pitches
   static constexpr int tile_k_bytes = kTile * k_pitch;
   static constexpr int tile_bytes = tile_k_bytes + kTile * v_pitch;
+  // streamed prefill: a ring of tile buffers filled by direct global->LDS
+  // loads of 1 KB (64 lanes x 16 bytes) each; the pitches are whole 16-byte
+  // slots, so a tile is exactly k_slots + v_slots such loads
+  static constexpr int k_slots = k_pitch / 16;
+  static constexpr int v_slots = v_pitch / 16;
+  static constexpr int ring_loads = k_slots + v_slots;
+  static constexpr int ring_avail = kLdsMax - 64 - kPcacheEntries * 4;
+  static constexpr int ring_bufs = ring_avail / tile_bytes >= 4 ? 4 : ring_avail / tile_bytes;
   // per-wave softmax state exchanged at the end of the decode schedule
   static constexpr int red_floats = D / 2 + 2;         // acc registers + l + m, per lane
   static constexpr int red_bytes = red_floats * kWave * 4;
@@ -123,7 +130,7 @@ template <int D, bool FP8, int MODE>
 struct Lds {
   using G = Geo<D, FP8>;
   static constexpr int dec = G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
-  static constexpr int pre = 2 * G::tile_bytes;         // double-buffered K / V tiles
+  static constexpr int pre = (Block<MODE, D>::stream ? G::ring_bufs : 2) * G::tile_bytes;
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
   static constexpr int pcache_entries = kPcacheEntries;
@@ -141,6 +148,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has returned
+// (expcnt and lgkmcnt fields left at their "no wait" maxima).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // 8 fp8 e4m3 bytes (two dwords) -> 8 bf16, exact.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -373,8 +384,7 @@ constexpr float kRescaleSlack = 8.0f;
 // probabilities as bf16 PV B-operands.  c = softmax_scale * log2(e) (*
 // k_descale), c > 0.
 template <int D, int NS>
-__device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c,
-                                          bf16x8 (&pb)[NS][2]) {
+__device__ __forceinline__ void max_update(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c) {
   float mx = neg_inf();
 #pragma unroll
   for (int n = 0; n < NS; ++n)
@@ -392,6 +402,13 @@ __device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)
       for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
     st.m = m_new;
   }
+}
+
+// Probabilities of NS tiles under the current running max, added to the row
+// sum and packed as bf16 PV B-operands.
+template <int D, int NS>
+__device__ __forceinline__ void probs(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c,
+                                      bf16x8 (&pb)[NS][2]) {
   // nothing visible yet: reference 0 so that exp2(-inf) = 0 instead of NaN
   const float nref = st.m == neg_inf() ? 0.f : -st.m;
   float psum = 0.f;
@@ -410,6 +427,13 @@ __device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)
     pb[n][1] = pack_bf16x8(p + 8);
   }
   st.l += psum;
+}
+
+template <int D, int NS>
+__device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c,
+                                          bf16x8 (&pb)[NS][2]) {
+  max_update<D, NS>(st, s, c);
+  probs<D, NS>(st, s, c, pb);
 }
 
 // O^T += V^T P^T for NS tiles whose V rows start at row kb of the stage, for
@@ -636,7 +660,10 @@ template <int D, bool FP8, int MODE>
 __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
-  constexpr int NK = Gm::pre_keys_per_unit;
+  constexpr int NTH = Block<MODE, D>::threads;
+  // a loader unit: NK consecutive keys x one 16-byte chunk, one unit per thread
+  constexpr int NK = (kTile * Gm::chunks) / NTH > 0 ? (kTile * Gm::chunks) / NTH : 1;
+  constexpr int NUNITS = (kTile * Gm::chunks) / NK;
   constexpr int NCT = Block<MODE, D>::nct;               // 32-row column tiles per wave
   constexpr int NS = kTile / kSub;                       // score tiles per LDS tile
   const int lane = threadIdx.x & (kWave - 1);
@@ -659,6 +686,11 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
       qreg[ct][j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j))
                        : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
+  // Let the Q loads land here, once.  Vector-memory loads retire in order on
+  // one counter; if Q were still counted as outstanding at the first score
+  // product, the wait placed there (inside the tile loop) would also cover the
+  // K/V prefetch issued just before it, on every tile.
+  wait_vmem_all();
 
   const int klo = split * p.split_keys;
   int khi = min(L, klo + p.split_keys);
@@ -682,7 +714,7 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   for (int ct = 0; ct < NCT; ++ct) state_init(st[ct]);
 
   const int unit = threadIdx.x;
-  const bool loader = unit < Gm::pre_units;
+  const bool loader = unit < NUNITS;
   const int chunk = unit % Gm::chunks;
   const int kg = unit / Gm::chunks;
   u32x4 kr[NK], vr[NK];
@@ -778,8 +810,282 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   }
 }
 
+
 // ---------------------------------------------------------------------------
-// the kernel: work-item decode, then one of the two schedules
+// streamed prefill schedule (head dim <= 128): each of 8 waves owns 32 packed
+// query rows; 64-key K/V tiles stream through a ring of LDS buffers
+// ---------------------------------------------------------------------------
+
+// s_waitcnt vmcnt(N) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane l's 16 bytes from src
+// land at LDS address lds + 16 l (lds wave-uniform).  Written as asm so that
+// the compiler does not track it as an LDS write: it would otherwise wait for
+// every such load in flight before each transposing LDS read, including the
+// tiles fetched ahead.  No register receives data (nothing to be reused while
+// the load is in flight); completion is waited for explicitly (wait_vmem)
+// before the barrier that publishes a tile.
+__device__ __forceinline__ void dma_load_16(const uint8_t* src, uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
+// Workgroup barrier for the ring.  No memory fence: the K/V tiles arrive by
+// direct global->LDS loads whose completion each wave has already waited for
+// (a fence would wait for every load in flight, including the tiles fetched
+// ahead).  The empty asm statements keep the compiler from moving LDS
+// accesses across the barrier, and the wait retires this wave's LDS reads
+// before any wave may refill the buffer they read.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0): this wave's LDS reads have returned
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global->LDS loads of one 64-key tile.  The tile's LDS image (64 K
+// rows at k_pitch, then 64 V rows at v_pitch) is a run of 16-byte slots; load
+// i of the tile writes slots [64 i, 64 i + 64), lane l slot 64 i + l, so the
+// lane fetches whichever 16 bytes belong there: the chunk of its row, or for a
+// pad slot chunk 0 again (in bounds, never read).  Wave w issues loads w,
+// w + NW, ...; per load it keeps its lane's row in the tile (high half) and
+// the byte offset of its chunk in the row (low half) in one register.
+template <int D, bool FP8, int NW>
+struct TileLoads {
+  using Gm = Geo<D, FP8>;
+  static constexpr int per_wave = (Gm::ring_loads + NW - 1) / NW;
+  static constexpr int min_per_wave = Gm::ring_loads / NW;
+  static_assert(min_per_wave >= 1, "every wave issues loads of every tile");
+  uint32_t slot_rc[per_wave];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < per_wave; ++j) {
+      const int i = wave + j * NW;
+      const bool kreg = i < Gm::k_slots;
+      const int slot = 64 * (kreg ? i : i - Gm::k_slots) + lane;
+      const int per_row = kreg ? Gm::k_slots : Gm::v_slots;
+      const int row = slot / per_row;
+      const int ch = slot - row * per_row;
+      slot_rc[j] = ((uint32_t)row << 16) | (ch < Gm::chunks ? (uint32_t)ch * 16u : 0u);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
+                                        const PageWalk& w, int key0, uint8_t* buf, int wave) const {
+    const int slot_mask = (1 << w.shift) - 1;
+    // page ids of all loads first (one LDS round trip), then the loads
+    int key[per_wave], page[per_wave];
+#pragma unroll
+    for (int j = 0; j < per_wave; ++j) {
+      key[j] = min(key0 + (int)(slot_rc[j] >> 16), w.kend - 1);
+      page[j] = w.pcache[(key[j] >> w.shift) - w.first_page];
+    }
+#pragma unroll
+    for (int j = 0; j < per_wave; ++j) {
+      const int i = wave + j * NW;
+      if (i < Gm::ring_loads) {
+        const uint8_t* pool = i < Gm::k_slots ? kpool : vpool;
+        const uint8_t* src = pool + (int64_t)page[j] * w.page_bytes + w.head_off +
+                             ((uint32_t)(key[j] & slot_mask) * (uint32_t)w.row_stride_b + (slot_rc[j] & 0xFFFFu));
+        dma_load_16(src, buf + 1024 * i);
+      }
+    }
+  }
+};
+
+// Raw scores of the 32 keys whose K rows start at kl: one MFMA chain.
+template <int D, bool FP8, int KPITCH>
+__device__ __forceinline__ f32x16 qk_tile(const uint8_t* kl, const bf16x8 (&qreg)[D / 16], int lane) {
+  f32x16 s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) s = mfma32(k_operand<D, FP8, KPITCH>(kl, 0, j, lane), qreg[j], s);
+  return s;
+}
+
+// O^T += V^T P^T for the 32 keys whose V rows start at vl.
+template <int D, bool FP8, int VPITCH>
+__device__ __forceinline__ void pv_tile(SoftmaxState<D>& st, const bf16x8 (&pb)[1][2], const uint8_t* vl,
+                                        int lane) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) st.o[t] = mfma32(v_operand<FP8, VPITCH>(vl, 0, t, h, lane), pb[0][h], st.o[t]);
+}
+
+// One pipelined 32-key step of a wave: the score product of the NEXT step
+// (K rows at kl) interleaved with the exp work of THIS step (raw scores sc),
+// then this step's PV product (V rows at vl) interleaved with its row sum.
+// The instruction order is fixed with scheduling barriers: each MFMA is
+// preceded by the LDS read of the operand two MFMAs ahead and followed by its
+// share of the VALU work, so that one wave keeps its matrix core fed while its
+// VALU works through the softmax.
+template <int D, bool FP8, int KPITCH, int VPITCH>
+__device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
+                                            const uint8_t* kl, const uint8_t* vl,
+                                            const bf16x8 (&qreg)[D / 16], float c, int lane) {
+  constexpr int NQ = D / 16;            // score MFMAs (k-steps over the head dim)
+  constexpr int NT = D / 32;            // 32-wide d tiles of O
+  constexpr int NV = 2 * NT;            // PV MFMAs; operand v = (tile v % NT, half v / NT)
+  constexpr int EPQ = 16 / NQ;          // exps per score MFMA
+  const float nref = st.m == neg_inf() ? 0.f : -st.m;
+  bf16x8 ka[NQ];
+  bf16x8 va[NV];
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sn[i] = 0.f;
+  ka[0] = k_operand<D, FP8, KPITCH>(kl, 0, 0, lane);
+  ka[1] = k_operand<D, FP8, KPITCH>(kl, 0, 1, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    if (j + 2 < NQ) ka[j + 2] = k_operand<D, FP8, KPITCH>(kl, 0, j + 2, lane);
+    else va[j + 2 - NQ] = v_operand<FP8, VPITCH>(vl, 0, (j + 2 - NQ) % NT, (j + 2 - NQ) / NT, lane);
+    sn = mfma32(ka[j], qreg[j], sn);
+#pragma unroll
+    for (int e = 0; e < EPQ; ++e) {
+      const int i = j * EPQ + e;
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, nref));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 pb[2];
+  pb[0] = pack_bf16x8(p);
+  pb[1] = pack_bf16x8(p + 8);
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = p[i] + p[i + 8];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (v + 2 < NV) va[v + 2] = v_operand<FP8, VPITCH>(vl, 0, (v + 2) % NT, (v + 2) / NT, lane);
+    st.o[v % NT] = mfma32(va[v], pb[v / NT], st.o[v % NT]);
+    if (v == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] += q[i + 4];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += (q[0] + q[2]) + (q[1] + q[3]);
+}
+
+// Tiles are issued NB-2 ahead: at the top of tile t every wave has waited for
+// its loads of tiles t and t+1 and passed the barrier, so both are resident and
+// every wave is done with tile t-1, whose buffer then receives tile t+NB-1.
+// Within a tile each wave runs 32-key steps; step u issues the score product
+// of step u+1 (K rows of tile t or t+1) before the softmax and PV product of
+// step u, so the two products of a wave overlap its exp work.
+template <int D, bool FP8, int MODE>
+__device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
+                            const PageWalk& pw, int L, float c, float vdesc) {
+  using Gm = Geo<D, FP8>;
+  constexpr int NW = Block<MODE, D>::waves;
+  constexpr int NB = Gm::ring_bufs;
+  static_assert(NB >= 3 && NB <= 4, "ring of three or four tiles");
+  using TL = TileLoads<D, FP8, NW>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrows = rm.ntok * rm.G;
+  const int r0 = wave * kCols;
+  const int last_tok = max(rm.ntok - 1, 0);
+
+  // Q operands of this wave's rows, in registers
+  bf16x8 qreg[D / 16];
+  {
+    const int r = r0 + (lane & 31);
+    const bool ok = r < nrows;
+    const int tok = ok ? r / rm.G : 0;
+    const int h = rm.g * rm.G + (r - tok * rm.G);
+    const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+
+  int khi = L;
+  if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
+  const bool wave_active = r0 < nrows;
+  const int tok_a = min(r0 / rm.G, last_tok);
+  const int tok_b = min((r0 + kCols - 1) / rm.G, last_tok);
+  const int wave_kmax = !wave_active ? 0 : (p.causal ? min(khi, rm.pos0 + tok_b + 1) : khi);
+  const int wave_kfull = p.causal ? min(khi, rm.pos0 + tok_a + 1) : khi;   // keys < this visible to all rows
+  const int my_tok = min((r0 + (lane & 31)) / rm.G, last_tok);
+  const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;       // this lane's row sees keys < klim
+
+  SoftmaxState<D> st;
+  state_init(st);
+  TL tl;
+  tl.init(wave, lane);
+  PageWalk w = pw;
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = 0; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    // The Q loads (first chunk) overlapped the page-table reads; let them land
+    // here, once: vector-memory loads retire in order on one counter, and a Q
+    // load still counted as outstanding at the first score product would make
+    // the wait placed there (inside the tile loop) cover every tile's loads.
+    wait_vmem_all();
+    __syncthreads();
+    const int ntiles = (ce - cb + kTile - 1) / kTile;
+    const int kvis = min(wave_kmax, ce) - cb;                     // this wave's keys in the chunk
+    const int nsub = kvis > 0 ? (kvis + kSub - 1) / kSub : 0;     // its 32-key steps
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t)
+      if (t < ntiles) tl.issue(p.k_pool, p.v_pool, w, cb + t * kTile, smem + t * Gm::tile_bytes, wave);
+    // Step u (u = -1 .. nsub-1) issues the scores of step u+1 and the softmax
+    // and PV product of step u.  Step -1 has no keys of its own (scores -inf,
+    // probabilities 0, its PV product adds nothing) and the scores issued by
+    // the last step are dropped, so every step runs the same code.
+    f32x16 s_cur;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_cur[i] = neg_inf();
+    int u = -1;
+    for (int t = 0; t < ntiles; ++t) {
+      if (NB == 4 && t + 2 < ntiles)
+        wait_vmem<TL::min_per_wave>();      // tile t+2 may stay in flight
+      else
+        wait_vmem<0>();
+      ring_barrier();
+      if (t + NB - 1 < ntiles)
+        tl.issue(p.k_pool, p.v_pool, w, cb + (t + NB - 1) * kTile, smem + ((t + NB - 1) % NB) * Gm::tile_bytes,
+                 wave);
+      // steps 2t and 2t+1 read tiles t and t+1 (step -1 also reads tile 0)
+      const int u_end = min(2 * t + 2, nsub);
+#pragma unroll 1
+      for (; u < u_end; ++u) {
+        const int tk = (u + 1) >> 1;                        // tile of step u+1's keys
+        const int tv = max(u, 0) >> 1;                      // tile of step u's keys
+        const uint8_t* kl = smem + (tk % NB) * Gm::tile_bytes + ((u + 1) & 1) * kSub * Gm::k_pitch;
+        const uint8_t* vl = smem + (tv % NB) * Gm::tile_bytes + Gm::tile_k_bytes + (u & 1) * kSub * Gm::v_pitch;
+        f32x16 sn[1];
+        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch>(st, s_cur, sn[0], kl, vl, qreg, c, lane);
+        if (u + 1 < nsub) {
+          const int k1 = cb + (u + 1) * kSub;
+          if (k1 + kSub > wave_kfull) mask_tile(sn[0], k1, klim, lane);
+          max_update<D, 1>(st, sn, c);
+        }
+        s_cur = sn[0];
+      }
+    }
+  }
+  if (wave_active) {
+    const float l_tot = st.l + xor32(st.l);
+    write_rows<D>(p, st, l_tot, r0, rm, 0, vdesc, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel: work-item decode, then one of the schedules
 // ---------------------------------------------------------------------------
 
 template <int D, bool FP8, int MODE>
@@ -868,7 +1174,10 @@ void attn_kernel(AttnParams p) {
   if constexpr (MODE == kDecode) {
     keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
-    rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
+    if constexpr (Block<MODE, D>::stream)
+      stream_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, c, vdesc);
+    else
+      rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
     if (q_len * p.group <= kCols)
       keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
@@ -968,11 +1277,21 @@ int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
   return 0;
 }
 
-int prefill_block_rows(int head_dim) {
+template <int D>
+int block_rows_d(Mode mode) {
+  switch (mode) {
+    case kDecode: return Block<kDecode, D>::waves * Block<kDecode, D>::nct * kCols;
+    case kPrefill: return Block<kPrefill, D>::waves * Block<kPrefill, D>::nct * kCols;
+    case kMixed: return Block<kMixed, D>::waves * Block<kMixed, D>::nct * kCols;
+  }
+  return 0;
+}
+
+int block_rows(int head_dim, Mode mode) {
   switch (head_dim) {
-    case 64: return Block<kPrefill, 64>::waves * Block<kPrefill, 64>::nct * kCols;
-    case 128: return Block<kPrefill, 128>::waves * Block<kPrefill, 128>::nct * kCols;
-    case 256: return Block<kPrefill, 256>::waves * Block<kPrefill, 256>::nct * kCols;
+    case 64: return block_rows_d<64>(mode);
+    case 128: return block_rows_d<128>(mode);
+    case 256: return block_rows_d<256>(mode);
   }
   return 0;
 }

@@ -111,7 +111,7 @@ def test_prefill_block_shape():
     for D, G in ((64, 2), (128, 4), (256, 32)):
         p = B.pa_plan(desc(head_dim=D, num_q_heads=8 * G, num_kv_heads=8))
         info = B.pa_plan_get_info(p)
-        assert info.group == G and info.q_block_tokens >= 1
+        assert info.group == G and info.q_block_tokens >= 1 and info.mixed_q_block_tokens >= 1
         B.pa_plan_destroy(p)
 
 
