@@ -104,14 +104,17 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   p->rows_cap = std::max(d.max_total_q, d.num_seqs);
 
   // Split-KV factor.  Work items of a decode/mixed launch: one per (q-block,
-  // KV head).  Split until there are about four workgroups per compute unit,
-  // but never into windows shorter than kMinSplitKeys keys.
+  // KV head).  Split until every compute unit has about two rounds of the
+  // workgroups it holds at once (each split adds a workgroup prologue and
+  // partial-result traffic; fewer leave the tail unbalanced), but never into
+  // windows shorter than kMinSplitKeys keys.
   const int64_t max_len = d.max_seq_len ? d.max_seq_len : capacity;
   int splits = d.num_splits;
   if (splits == 0) {
     const int64_t qblocks = std::max<int64_t>(1, ceil_div(d.max_total_q, p->mixed_q_block_tokens));
     const int64_t items = std::max<int64_t>(1, std::max<int64_t>(d.num_seqs, qblocks)) * d.num_kv_heads;
-    const int64_t want = ceil_div(4 * (int64_t)cus, items);
+    const int64_t resident = pa::workgroups_per_cu(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3, pa::kDecode);
+    const int64_t want = ceil_div(2 * resident * (int64_t)cus, items);
     const int64_t by_len = std::max<int64_t>(1, max_len / kMinSplitKeys);
     splits = (int)std::max<int64_t>(1, std::min(want, by_len));
   }

@@ -69,6 +69,9 @@ hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnPara
 hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream);
 // LDS bytes the attention instance uses (host-side check).
 int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode);
+// Workgroups of the attention instance that fit on one compute unit at once
+// (by LDS and by waves per SIMD).
+int workgroups_per_cu(int head_dim, bool kv_fp8, Mode mode);
 // Packed query rows (tokens x GQA heads) per workgroup of a launch mode.
 int block_rows(int head_dim, Mode mode);
 

@@ -122,7 +122,7 @@ struct Geo {
   static constexpr int ring_avail = kLdsMax - 64 - kPcacheEntries * 4;
   static constexpr int ring_bufs = ring_avail / tile_bytes >= 4 ? 4 : ring_avail / tile_bytes;
   // per-wave softmax state exchanged at the end of the decode schedule
-  static constexpr int red_floats = D / 2 + 2;         // acc registers + l + m, per lane
+  static constexpr int red_floats = D / 2 + 4;         // acc registers + (l, m) record, per lane
   static constexpr int red_bytes = red_floats * kWave * 4;
 };
 
@@ -524,44 +524,62 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrows = rm.ntok * rm.G;
 
-  // stage the block's query rows (zero padded to 32) in LDS
-  uint8_t* ql = smem;
-  {
-    constexpr int cpr = D * 2 / 16;
-    for (int u = threadIdx.x; u < kCols * cpr; u += Block<MODE, D>::threads) {
-      const int r = u / cpr, ch = u % cpr;
-      u32x4 v{0u, 0u, 0u, 0u};
-      if (r < nrows) {
-        const int tok = r / rm.G;
-        const int h = rm.g * rm.G + (r - tok * rm.G);
-        v = *reinterpret_cast<const u32x4*>(p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t +
-                                            (int64_t)h * D + ch * 8);
-      }
-      *reinterpret_cast<u32x4*>(ql + r * Gm::q_pitch + ch * 16) = v;
-    }
-  }
-  __syncthreads();
-
   // key window of this split, clipped by the causal limit of the last token
   const int klo = split * p.split_keys;
   int khi = min(L, klo + p.split_keys);
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
+
+  SoftmaxState<D> st[1];
+  state_init(st[0]);
+  if (khi <= klo) {
+    // empty window: the (partial) rows are empty, nothing to stage or stream
+    if (wave == 0) write_rows<D>(p, st[0], 0.f, 0, rm, split, vdesc, lane);
+    return;
+  }
+
+  // The block's query rows (zero padded to 32) and the page ids of the first
+  // chunk of keys are fetched together and published with one barrier.
+  uint8_t* ql = smem;
+  PageWalk w = pw;
+  const int chunk_keys = kPcacheEntries << w.shift;
+  {
+    constexpr int cpr = D * 2 / 16;
+    constexpr int NTH = Block<MODE, D>::threads;
+    constexpr int QPT = (kCols * cpr + NTH - 1) / NTH;   // 16-byte Q chunks per thread
+    u32x4 qv[QPT];
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int u = threadIdx.x + k * NTH;
+      const int r = u / cpr, ch = u % cpr;
+      qv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (u < kCols * cpr && r < nrows) {
+        const int tok = r / rm.G;
+        const int h = rm.g * rm.G + (r - tok * rm.G);
+        qv[k] = *reinterpret_cast<const u32x4*>(p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t +
+                                                (int64_t)h * D + ch * 8);
+      }
+    }
+    fill_pcache(w, pcache, klo, min(khi, klo + chunk_keys));
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int u = threadIdx.x + k * NTH;
+      if (u < kCols * cpr) *reinterpret_cast<u32x4*>(ql + (u / cpr) * Gm::q_pitch + (u % cpr) * 16) = qv[k];
+    }
+  }
+  __syncthreads();
   // this lane's query row sees keys < klim
   const int my_tok = min((lane & 31) / rm.G, max(rm.ntok - 1, 0));
   const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;
   // keys below kfull are visible to every row of the block
   const int kfull = p.causal ? min(khi, rm.pos0 + 1) : khi;
 
-  SoftmaxState<D> st[1];
-  state_init(st[0]);
-
-  PageWalk w = pw;
-  const int chunk_keys = kPcacheEntries << w.shift;
   for (int cb = klo; cb < khi; cb += chunk_keys) {
     const int ce = min(khi, cb + chunk_keys);
-    __syncthreads();
-    fill_pcache(w, pcache, cb, ce);
-    __syncthreads();
+    if (cb != klo) {
+      __syncthreads();
+      fill_pcache(w, pcache, cb, ce);
+      __syncthreads();
+    }
     constexpr int STEP = Gm::dec_step;
     constexpr int NT = Gm::dec_tiles;
     const int nsub = (ce - cb + STEP - 1) / STEP;
@@ -618,20 +636,23 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     const int cnt = half < nbuf ? half : nbuf;
     const int w_lo = active - cnt;         // writers [w_lo, active)
     const int r_lo = active - 2 * cnt;     // readers [r_lo, w_lo)
+    // a wave's state as 16-byte records [record][lane]: O in D/8 records, then (l, m)
     if (wave >= w_lo && wave < active) {
-      float* buf = red + (wave - w_lo) * Gm::red_floats * kWave;
+      f32x4* buf = reinterpret_cast<f32x4*>(red + (wave - w_lo) * Gm::red_floats * kWave);
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) buf[(t * 16 + i) * kWave + lane] = st[0].o[t][i];
-      buf[(D / 2) * kWave + lane] = st[0].l;
-      buf[(D / 2 + 1) * kWave + lane] = st[0].m;
+        for (int q = 0; q < 4; ++q)
+          buf[(4 * t + q) * kWave + lane] = f32x4{st[0].o[t][4 * q], st[0].o[t][4 * q + 1],
+                                                  st[0].o[t][4 * q + 2], st[0].o[t][4 * q + 3]};
+      buf[(D / 8) * kWave + lane] = f32x4{st[0].l, st[0].m, 0.f, 0.f};
     }
     __syncthreads();
     if (wave >= r_lo && wave < w_lo) {
-      const float* buf = red + (wave - r_lo) * Gm::red_floats * kWave;
-      const float l2 = buf[(D / 2) * kWave + lane];
-      const float m2 = buf[(D / 2 + 1) * kWave + lane];
+      const f32x4* buf = reinterpret_cast<const f32x4*>(red + (wave - r_lo) * Gm::red_floats * kWave);
+      const f32x4 lm = buf[(D / 8) * kWave + lane];
+      const float l2 = lm[0];
+      const float m2 = lm[1];
       const float mm = fmaxf(st[0].m, m2);
       const float ref = mm == neg_inf() ? 0.f : mm;
       const float a1 = __builtin_amdgcn_exp2f(st[0].m - ref);
@@ -639,7 +660,11 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
       for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[0].o[t][i] = st[0].o[t][i] * a1 + buf[(t * 16 + i) * kWave + lane] * a2;
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = buf[(4 * t + q) * kWave + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st[0].o[t][4 * q + e] = st[0].o[t][4 * q + e] * a1 + v[e] * a2;
+        }
       st[0].l = st[0].l * a1 + l2 * a2;
       st[0].m = mm;
     }
@@ -1266,6 +1291,33 @@ hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnPara
     case 256: return kv_fp8 ? launch_mode<256, true>(mode, p, grid, stream) : launch_mode<256, false>(mode, p, grid, stream);
   }
   return hipErrorInvalidValue;
+}
+
+template <int D, bool FP8, int MODE>
+constexpr int wgs_per_cu() {
+  constexpr int by_lds = kLdsMax / Lds<D, FP8, MODE>::bytes;
+  constexpr int by_waves = Block<MODE, D>::waves_per_eu * 4 / Block<MODE, D>::waves;   // 4 SIMDs per CU
+  constexpr int n = by_lds < by_waves ? by_lds : by_waves;
+  return n > 0 ? n : 1;
+}
+
+template <int D, bool FP8>
+int wgs_mode(Mode mode) {
+  switch (mode) {
+    case kDecode: return wgs_per_cu<D, FP8, kDecode>();
+    case kPrefill: return wgs_per_cu<D, FP8, kPrefill>();
+    case kMixed: return wgs_per_cu<D, FP8, kMixed>();
+  }
+  return 1;
+}
+
+int workgroups_per_cu(int head_dim, bool kv_fp8, Mode mode) {
+  switch (head_dim) {
+    case 64: return kv_fp8 ? wgs_mode<64, true>(mode) : wgs_mode<64, false>(mode);
+    case 128: return kv_fp8 ? wgs_mode<128, true>(mode) : wgs_mode<128, false>(mode);
+    case 256: return kv_fp8 ? wgs_mode<256, true>(mode) : wgs_mode<256, false>(mode);
+  }
+  return 1;
 }
 
 int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
