@@ -38,8 +38,14 @@ LSE_TOL = 1e-3
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and blank space removed, so
+    that a recorded profile stays attached to the code it measured."""
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def read_traffic(workload: str):

@@ -20,10 +20,11 @@
 //     per-lane reduction plus one exchange with lane^32, the running rescale
 //     factor is a per-lane scalar, and the probabilities P^T are already in the
 //     B-operand layout of the second product O^T += V^T P^T (no shuffle of P).
-//   * V^T (head_dim x keys) is produced while staging V into LDS: each lane
-//     loads 16-byte rows of several consecutive keys and writes them back
-//     transposed, so the PV A-operand is two 8-byte (bf16) / 4-byte (fp8) LDS
-//     reads per MFMA.
+//   * V stays row-major in LDS; the PV A-operand (8 consecutive keys of one
+//     head-dim column per lane) comes from the LDS unit's transposing reads
+//     (ds_read_b64_tr_b16 / _tr_b8).  K rows are permuted inside a 32-key
+//     score tile so that each lane's probabilities for one PV k-step are
+//     exactly those 8 consecutive keys.
 //   * fp8 e4m3 K/V stay fp8 in LDS and are widened to bf16 in registers right
 //     before each MFMA with v_cvt_scalef32_pk_bf16_fp8 (exact: e4m3 is a subset
 //     of bf16); k_descale is folded into the score scale, v_descale into the
@@ -32,13 +33,19 @@
 //     sub-tiles of one (sequence, KV head, split), each wave staging its own
 //     sub-tile through a private LDS region with register prefetch of the next
 //     one, and the per-wave softmax states are merged through LDS at the end.
-//   * Prefill schedule: each wave owns 32 packed query rows; 64-key K/V tiles
-//     are loaded cooperatively into LDS (register prefetch of the next tile)
-//     and read by every wave; causal sub-tiles above a wave's diagonal are
-//     skipped, and only diagonal/tail sub-tiles are masked.
-//   * Slots past seq_lens[b] are never loaded (zero-filled instead), page-table
-//     columns past the live page count are never read, and masked scores are
-//     selected to -inf, so poisoned cache contents cannot leak into outputs.
+//   * Streamed prefill schedule (head dim <= 128): 8 waves each own 32 packed
+//     query rows; 64-key K/V tiles stream through a ring of four LDS buffers
+//     filled by direct global->LDS loads two tiles ahead; each wave issues the
+//     score product of its next 32 keys before the softmax and PV product of
+//     the current ones.
+//   * Row-split schedule (mixed-batch q-blocks, head dim 256 prefill): 4 waves
+//     each own 32 rows; 64-key tiles double-buffered with register prefetch.
+//   * Causal sub-tiles above a wave's diagonal are skipped, and only
+//     diagonal/tail sub-tiles are masked.
+//   * Keys past seq_lens[b] are never loaded (loads clamp to the last live
+//     key), page-table columns past the live page count are never read, and
+//     masked scores are selected to -inf, so poisoned cache contents cannot
+//     leak into outputs.
 #include "pa_internal.h"
 
 namespace pa {
