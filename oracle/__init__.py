@@ -82,14 +82,17 @@ def load(path: str):
     L.pao_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                             vp, vp, vp, vp]
     L.pao_merge.restype = ctypes.c_int
+    L.pao_fp8_e4m3_encode.argtypes = [ctypes.c_double]
+    L.pao_fp8_e4m3_encode.restype = ctypes.c_uint8
+    L.pao_append.argtypes = [ctypes.POINTER(Problem), vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp]
+    L.pao_append.restype = ctypes.c_int
     return L
 
 
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
+        build(force=False)                  # compiles when missing or older than the source
         _lib = load(_LIB)
     return _lib
 
@@ -186,3 +189,43 @@ def merge(o_parts: np.ndarray, lse_parts: np.ndarray):
     if rc != 0:
         raise OracleError("pao_merge failed with code %d" % rc)
     return o, lse
+
+
+def fp8_e4m3_encode(x: float) -> int:
+    """Nearest finite E4M3 code to x (ties to an even mantissa), saturating; NaN keeps its sign."""
+    return int(lib().pao_fp8_e4m3_encode(float(x)))
+
+
+def append(*, k_new: np.ndarray, v_new: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+           page_table: np.ndarray, cu_new: np.ndarray, seq_lens: np.ndarray,
+           num_kv_heads: int, head_dim: int, page_size: int, kv_dtype: int = KV_BF16,
+           k_descale: float = 1.0, v_descale: float = 1.0, new_stride_t: int = 0,
+           kv_page_stride: int = 0, pt_cols: Optional[int] = None):
+    """KV-cache append (see pa_oracle.h).  Returns updated copies of the pools.
+
+    k_new, v_new : uint16 bf16 bits [T_new, Hkv, D] (or flat with new_stride_t)
+    k_pool, v_pool : uint16 (bf16 bits) or uint8 (fp8 codes), [P, page, Hkv, D]
+    cu_new   : int32 [B+1] offsets of each sequence's new tokens
+    seq_lens : int32 [B] lengths after the append
+    """
+    page_table = _c(page_table, np.int32)
+    cu_new = _c(cu_new, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    kv_np = np.uint16 if kv_dtype == KV_BF16 else np.uint8
+    k_out = np.array(k_pool, dtype=kv_np, copy=True, order="C")
+    v_out = np.array(v_pool, dtype=kv_np, copy=True, order="C")
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    per_page = kv_page_stride if kv_page_stride else page_size * num_kv_heads * head_dim
+    pr = Problem(num_seqs=seq_lens.shape[0], num_q_heads=num_kv_heads,
+                 num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                 num_pages=k_out.size // per_page,
+                 pt_cols=page_table.shape[1] if pt_cols is None else pt_cols,
+                 pt_row_stride=page_table.shape[1], kv_page_stride=kv_page_stride,
+                 q_stride_t=0, kv_dtype=kv_dtype, causal=1, scale=1.0,
+                 k_descale=k_descale, v_descale=v_descale)
+    rc = lib().pao_append(ctypes.byref(pr), _ptr(k_new), _ptr(v_new), int(new_stride_t),
+                          _ptr(page_table), _ptr(cu_new), _ptr(seq_lens), _ptr(k_out), _ptr(v_out))
+    if rc != 0:
+        raise OracleError("pao_append failed with code %d" % rc)
+    return k_out, v_out

@@ -224,3 +224,79 @@ int pao_merge(int32_t num_parts, int64_t n, int32_t head_dim,
   }
   return PAO_OK;
 }
+
+/*
+ * Nearest finite OCP FP8 E4M3 code to x, ties to the code with an even
+ * mantissa, magnitudes beyond the largest finite value (448) saturating to it;
+ * NaN gives the NaN pattern (all exponent and mantissa bits set) with x's sign.
+ * Written as a search over the 127 finite non-negative codes so that it rests
+ * on the decoder above and nothing else.
+ */
+uint8_t pao_fp8_e4m3_encode(double x) {
+  const int neg = signbit(x) != 0;
+  if (isnan(x)) return (uint8_t)(0x7F | (neg ? 0x80 : 0));   /* E4M3's only NaN pattern */
+  const double a = fabs(x);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c < 0x7F; ++c) {            /* 0x7F is NaN */
+    const double err = fabs(pao_fp8_e4m3_to_double((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+/*
+ * KV-cache append.  The new tokens of sequence b are rows cu_new[b] ..
+ * cu_new[b+1]-1 of k_new / v_new; they are the LAST n_b tokens of the
+ * sequence whose length (after the append) is seq_lens[b], so new token i
+ * goes to position L - n_b + i: physical page page_table[b][pos / page],
+ * slot pos % page, head g.  bf16 pools receive the bits unchanged; fp8 pools
+ * receive the E4M3 code nearest to the binary32 quotient value / descale
+ * (the stored code times the descale reproduces the value, as for reads).
+ * Nothing else in the pools is written.  (The fused preprocessing of
+ * TensorRT-LLM PR #17399, section "Planning, preprocessing, and workspace
+ * ownership", appends the step's K/V to the paged cache before attention.)
+ */
+int pao_append(const pao_problem* pr, const uint16_t* k_new, const uint16_t* v_new,
+               int64_t new_stride_t, const int32_t* page_table, const int32_t* cu_new,
+               const int32_t* seq_lens, void* k_pool, void* v_pool) {
+  int rc = check_problem(pr);
+  if (rc != PAO_OK) return rc;
+  if (!k_new || !v_new || !page_table || !cu_new || !seq_lens || !k_pool || !v_pool)
+    return PAO_ERR_ARG;
+  rc = check_metadata(pr, page_table, cu_new, seq_lens);
+  if (rc != PAO_OK) return rc;
+  const int64_t D = pr->head_dim, H = pr->num_kv_heads;
+  const int64_t stride = new_stride_t ? new_stride_t : H * D;
+  const int64_t page_stride =
+      pr->kv_page_stride ? pr->kv_page_stride : (int64_t)pr->page_size * H * D;
+  const float kd = (float)pr->k_descale, vd = (float)pr->v_descale;
+  for (int32_t b = 0; b < pr->num_seqs; ++b) {
+    const int64_t n = (int64_t)cu_new[b + 1] - cu_new[b];
+    const int64_t L = seq_lens[b];
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t t = cu_new[b] + i;
+      const int64_t pos = L - n + i;
+      const int64_t page = page_table[(int64_t)b * pr->pt_row_stride + pos / pr->page_size];
+      const int64_t slot = pos % pr->page_size;
+      for (int64_t g = 0; g < H; ++g)
+        for (int64_t d = 0; d < D; ++d) {
+          const int64_t src = t * stride + g * D + d;
+          const int64_t dst = page * page_stride + (slot * H + g) * D + d;
+          if (pr->kv_dtype == PAO_KV_BF16) {
+            ((uint16_t*)k_pool)[dst] = k_new[src];
+            ((uint16_t*)v_pool)[dst] = v_new[src];
+          } else {
+            const float kq = (float)pao_bf16_to_double(k_new[src]) / kd;
+            const float vq = (float)pao_bf16_to_double(v_new[src]) / vd;
+            ((uint8_t*)k_pool)[dst] = pao_fp8_e4m3_encode((double)kq);
+            ((uint8_t*)v_pool)[dst] = pao_fp8_e4m3_encode((double)vq);
+          }
+        }
+    }
+  }
+  return PAO_OK;
+}

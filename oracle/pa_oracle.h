@@ -112,6 +112,27 @@ int pao_merge(int32_t num_parts, int64_t n, int32_t head_dim,
               const double* o_parts, const double* lse_parts,
               double* o, double* lse);
 
+/*
+ * Nearest finite OCP FP8 E4M3 code to x (ties to an even mantissa),
+ * saturating to +-448.  x must not be NaN.
+ */
+uint8_t pao_fp8_e4m3_encode(double x);
+
+/*
+ * KV-cache append: new token i of sequence b (row cu_new[b] + i of k_new and
+ * v_new, bf16 bits, new_stride_t elements between tokens, 0 = Hkv*D) is the
+ * token at position seq_lens[b] - n_b + i, where n_b = cu_new[b+1] - cu_new[b]
+ * and seq_lens holds the lengths after the append.  Its rows are written to
+ * k_pool / v_pool at that position's (page, slot) for every KV head: bf16
+ * bits unchanged, or for fp8 pools the E4M3 code nearest to the binary32
+ * quotient value / descale (pr->k_descale, pr->v_descale taken as binary32).
+ * pr->num_q_heads, scale and causal are not used.  Returns PAO_ERR_DATA for
+ * metadata that breaks the contract (n_b > L, L > C*page, page id out of range).
+ */
+int pao_append(const pao_problem* pr, const uint16_t* k_new, const uint16_t* v_new,
+               int64_t new_stride_t, const int32_t* page_table, const int32_t* cu_new,
+               const int32_t* seq_lens, void* k_pool, void* v_pool);
+
 #ifdef __cplusplus
 }
 #endif

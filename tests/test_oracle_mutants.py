@@ -22,7 +22,8 @@ MUTANTS = {
     "scale_dropped": ("s[j - lo] = pr->scale * dot;", "s[j - lo] = dot;"),
     "slot_shift": ("const int64_t slot = j % pr->page_size;\n    double dot",
                    "const int64_t slot = (j + 1) % pr->page_size;\n    double dot"),
-    "kv_head_slot_swapped": ("(slot * H + g) * D + d", "(g * pr->page_size + slot) * D + d"),
+    "kv_head_slot_swapped": ("const int64_t idx = page * page_stride + (slot * H + g) * D + d;",
+                             "const int64_t idx = page * page_stride + (g * pr->page_size + slot) * D + d;"),
     "fp8_bias": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
                  "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     "fp8_subnormal": ("mag = ldexp((double)m / 8.0, 1 - 7);", "mag = ldexp((double)m / 8.0, -7);"),
