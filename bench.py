@@ -3,9 +3,16 @@
 Headline line: the decode workload (B=256, Hq/Hkv 32/8, D 128, page 16,
 seq_lens U[1024, 2048], bf16 K/V) through pa_run_decode, reported as KV GB/s
 and as a fraction of the 8 TB/s HBM3E roof.  The other full-size workloads
-(causal varlen prefill, unified mixed batch, fp8 long-context decode) are
-timed too and reported under "secondary".  Every workload is validated
-against the fp64 oracle on sampled rows before it is timed.
+(causal varlen prefill, unified mixed batch, fp8 long-context decode) and
+the KV-cache append of the mixed batch's new tokens are timed too and
+reported under "secondary".
+
+The CPU leg (skipped with --no-cpu) is the only part that runs the fp64
+oracle: it checks sampled rows of every timed attention workload against the
+GPU output and times the oracle on a bounded sample of the headline workload
+("cpu_baseline").  The append is checked without the oracle: every appended
+element must equal the new row (bf16) or torch's own E4M3 cast of the
+binary32 quotient (fp8), and nothing else in the pools may change.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-secondary] [--no-cpu]
 
@@ -87,12 +94,12 @@ def time_steps(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps       # ms per step
 
 
-def bench_workload(name, mode, steps, warmup, sample_rows_per_seq=2, heads=2):
-    """Generate, validate on sampled rows, time.  Returns a result dict."""
+def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, heads=2):
+    """Generate, time, and (CPU leg) check sampled rows.  Returns a result dict."""
     import torch
+    from paged_kv_gqa_attention_amd import binding as B
     from paged_kv_gqa_attention_amd import synth
     from paged_kv_gqa_attention_amd.attention import DeviceInputs, PagedAttention
-    from tests import helpers as H
 
     t0 = time.time()
     w = synth.WORKLOADS[name]()
@@ -102,17 +109,12 @@ def bench_workload(name, mode, steps, warmup, sample_rows_per_seq=2, heads=2):
     out, lse = pa.new_outputs(x)
     stream = torch.cuda.current_stream()
     args = pa.args(x, out, lse)
-    from paged_kv_gqa_attention_amd import binding as B
     run = {"prefill": B.pa_run_prefill, "decode": B.pa_run_decode, "mixed": B.pa_run_mixed}[mode]
     s_ptr = int(stream.cuda_stream)
 
     def step():
         run(pa.plan, args, s_ptr)
 
-    step()
-    torch.cuda.synchronize()
-    rows = synth.sample_rows(w, per_seq=sample_rows_per_seq, heads=heads)
-    ok, eo, el = validate(w, out, lse, rows, H.run_oracle(w, rows=rows))
     ms = time_steps(step, steps, warmup, stream)
     kv = w.kv_bytes()
     qo = w.qo_bytes()
@@ -124,15 +126,88 @@ def bench_workload(name, mode, steps, warmup, sample_rows_per_seq=2, heads=2):
         "alg_gbs": (kv + qo) / (ms * 1e-3) / 1e9,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "num_splits": int(pa.info.num_splits),
-        "validated_rows": len(rows), "max_abs_err_o": eo, "max_abs_err_lse": el,
-        "valid": ok, "gen_s": round(gen_s, 2), "w": w,
+        "validated_rows": 0, "max_abs_err_o": None, "max_abs_err_lse": None,
+        "valid": None, "gen_s": round(gen_s, 2), "w": w,
     }
+    if cpu_leg:
+        rows = synth.sample_rows(w, per_seq=sample_rows_per_seq, heads=heads)
+        ok, eo, el = oracle_check(w, out, lse, rows)
+        res.update(validated_rows=len(rows), max_abs_err_o=eo, max_abs_err_lse=el, valid=ok)
     return res
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The oracle, untuned, on a bounded sample: whole sequences (all heads) in
-    order until about budget_s seconds of work; reports KV GB/s over the sample."""
+def bench_append(kv_dtype, steps, warmup):
+    """pa_run_append of the mixed batch's new tokens (8 chunks of 1000 plus 248
+    decode tokens, Hkv 8, D 128, page 16).  Algorithmic bytes per launch: the
+    new K and V rows read as bf16 plus the same elements written in the pool's
+    dtype.  Checked by properties that hold at any size (no oracle)."""
+    import torch
+    from paged_kv_gqa_attention_amd import binding as B
+    from paged_kv_gqa_attention_amd import synth
+    from paged_kv_gqa_attention_amd.attention import DeviceInputs, PagedAttention
+
+    w = synth.mixed_24b(kv_dtype=kv_dtype)
+    x = DeviceInputs(w)
+    pa = PagedAttention(w)
+    T, Hkv, D = w.total_q, w.num_kv_heads, w.head_dim
+    n = T * Hkv * D
+    k_new = synth.normal_bf16(n, 11, 1).view(T, Hkv, D).cuda()
+    v_new = synth.normal_bf16(n, 11, 2).view(T, Hkv, D).cuda()
+    k_before, v_before = x.k_pool.clone(), x.v_pool.clone()
+    a = B.make_append_args(k_new=k_new, v_new=v_new, cu_new=x.cu_q_lens, seq_lens=x.seq_lens,
+                           page_table=x.page_table, k_pool=x.k_pool, v_pool=x.v_pool,
+                           k_descale=x.k_descale, v_descale=x.v_descale)
+    stream = torch.cuda.current_stream()
+    s_ptr = int(stream.cuda_stream)
+
+    def step():
+        B.pa_run_append(pa.plan, a, s_ptr)
+
+    ms = time_steps(step, steps, warmup, stream)
+    # where every new token lands
+    cu = w.cu_q_lens.numpy().astype(np.int64)
+    L = w.seq_lens.numpy().astype(np.int64)
+    seq = np.repeat(np.arange(w.num_seqs), np.diff(cu))
+    pos = L[seq] - (cu[seq + 1] - cu[seq]) + (np.arange(T) - cu[seq])
+    pages = torch.from_numpy(w.page_table.numpy()[seq, pos // w.page_size].astype(np.int64)).cuda()
+    slots = torch.from_numpy((pos % w.page_size).astype(np.int64)).cuda()
+    ok = True
+    for new, pool, before, d in ((k_new, x.k_pool, k_before, w.k_descale),
+                                 (v_new, x.v_pool, v_before, w.v_descale)):
+        got = pool[pages, slots].cpu()
+        if kv_dtype == "bf16":
+            ok &= bool(torch.equal(got.view(torch.int16), new.cpu().view(torch.int16)))
+        else:
+            # the IEEE binary32 quotient (numpy divides exactly; torch on the GPU
+            # multiplies by the divisor's reciprocal), then torch's RNE cast
+            quot = new.cpu().float().numpy() / np.float32(d)
+            want = torch.from_numpy(np.clip(quot, -448.0, 448.0)).to(torch.float8_e4m3fn)
+            ok &= bool(torch.equal(got, want.view(torch.uint8)))
+        rest = pool.clone()
+        rest[pages, slots] = before[pages, slots]
+        ok &= bool(torch.equal(rest.view(torch.uint8), before.view(torch.uint8)))
+    esz = 2 if kv_dtype == "bf16" else 1
+    alg = 2 * n * 2 + 2 * n * esz
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": "append_mixed_24b_" + kv_dtype, "entry": "pa_run_append",
+            "ms_per_step": ms, "new_tokens": T, "alg_bytes": alg, "alg_gbs": gbs,
+            "bound": "hbm", "roofline_frac": gbs / HBM_PEAK_GBS, "valid": ok}
+
+
+# ---------------------------------------------------------------------------
+# CPU leg: the only code here that runs the oracle
+# ---------------------------------------------------------------------------
+
+def oracle_check(w, out, lse, rows):
+    """Compare sampled output rows with the fp64 oracle's."""
+    from tests import helpers as H
+    return validate(w, out, lse, rows, H.run_oracle(w, rows=rows))
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The oracle, untuned, on a bounded sample: groups of 16 whole sequences
+    (all heads), in order and wrapping round, until about budget_s seconds of
+    work; reports KV GB/s over the sample."""
     from tests import helpers as H
     Hq = w.num_q_heads
     cu = w.cu_q_lens.numpy()
@@ -140,7 +215,7 @@ def cpu_baseline(w, budget_s=20.0):
     threads = os.cpu_count() or 1
     done_bytes, elapsed, nseq = 0, 0.0, 0
     b = 0
-    while b < w.num_seqs and elapsed < budget_s:
+    while elapsed < budget_s:
         take = min(w.num_seqs - b, 16)
         rows = np.arange(cu[b] * Hq, cu[b + take] * Hq, dtype=np.int64)
         t = time.time()
@@ -149,11 +224,11 @@ def cpu_baseline(w, budget_s=20.0):
         done_bytes += int(L[b:b + take].sum()) * w.num_kv_heads * w.head_dim * 2 * \
             (2 if w.kv_dtype == "bf16" else 1)
         nseq += take
-        b += take
+        b = (b + take) % w.num_seqs
     return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d sequences (all %d query heads), %.1f s of fp64 CPU work"
-                      % (nseq, w.num_seqs, Hq, elapsed)}
+            "sample": "%d sequence passes over the %d-sequence batch (all %d query heads), "
+                      "%.1f s of fp64 CPU work" % (nseq, w.num_seqs, Hq, elapsed)}
 
 
 def main():
@@ -192,19 +267,23 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "repeats": 5}), flush=True)
         return
+    cpu_leg = not a.no_cpu
     if a.only:
-        r = bench_workload(a.only, modes[a.only], a.steps, a.warmup)
+        if a.only.startswith("append_"):
+            r = bench_append(a.only[len("append_"):], a.steps, a.warmup)
+        else:
+            r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg)
         print(json.dumps(strip(r)), flush=True)
         return
 
-    prim = bench_workload("decode_llama8b", "decode", a.steps, a.warmup)
-    print("# primary validated=%s err_o=%.3g err_lse=%.3g ms=%.4f" % (
+    prim = bench_workload("decode_llama8b", "decode", a.steps, a.warmup, cpu_leg)
+    print("# primary validated=%s err_o=%s err_lse=%s ms=%.4f" % (
         prim["valid"], prim["max_abs_err_o"], prim["max_abs_err_lse"], prim["ms_per_step"]),
         file=sys.stderr, flush=True)
     sec = {}
     if not a.no_secondary:
         for name in ("prefill_causal", "mixed_24b", "decode_fp8_long"):
-            r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup)
+            r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup, cpu_leg)
             bound = "mfma" if name == "prefill_causal" else "hbm"
             if bound == "mfma":
                 frac = r["tflops"] / BF16_PEAK_TFLOPS
@@ -217,6 +296,12 @@ def main():
             e["roofline_frac"] = frac
             sec[name] = e
             print("# %s validated=%s ms=%.4f frac=%.3f" % (name, r["valid"], r["ms_per_step"], frac),
+                  file=sys.stderr, flush=True)
+        for kv in ("bf16", "fp8_e4m3"):
+            r = bench_append(kv, a.steps, a.warmup)
+            sec[r["workload"]] = r
+            print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
+                                                           r["roofline_frac"]),
                   file=sys.stderr, flush=True)
     w = prim["w"]
     alg_bytes = prim["kv_bytes"] + prim["qo_bytes"]

@@ -206,6 +206,48 @@ pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream)
  * decode. */
 pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
+/*
+ * KV-cache append (the step before attention): write the K and V rows of a
+ * step's new tokens into the paged pools, as the fused preprocessing of
+ * TensorRT-LLM PR #17399 does before its kernels run (section "Planning,
+ * preprocessing, and workspace ownership": QKV extraction, RoPE, KV-cache
+ * append, page metadata).
+ *   k_new, v_new  bf16 [T_new, Hkv, D], head_dim contiguous, 16-byte aligned;
+ *                 new_stride_t elements between tokens (0 = Hkv*D), multiple of 8
+ *   cu_new        int32 [B+1]: sequence b's new tokens are rows
+ *                 cu_new[b] .. cu_new[b+1]-1 (cu_new[B] <= the plan's max_total_q)
+ *   seq_lens      int32 [B]: lengths AFTER the append; new token i of sequence b
+ *                 is position seq_lens[b] - n_b + i (n_b = cu_new[b+1] - cu_new[b]),
+ *                 the same "queries are the last tokens" convention as the runs
+ *   page_table, k_pool, v_pool  as in pa_args (written, not read, at those
+ *                 positions; page ids must be valid for every appended position)
+ *   k_descale, v_descale  fp8 pools only: device fp32 scalars; the stored code is
+ *                 the E4M3 value nearest to (binary32) value / descale, ties to an
+ *                 even mantissa, saturating at +-448 (NaN gives the NaN code, sign kept)
+ * Uses the plan's geometry (B, Hkv, D, page size, pool layout, KV dtype); Hq,
+ * splits and the workspace play no part.  Nothing else in the pools changes.
+ * A token whose position falls outside 0 .. page_table_cols * page - 1, or whose
+ * row is at or past max_total_q, breaks the contract and is skipped (the lengths
+ * live on the device, so no status reports it).  All buffers stay the caller's;
+ * the library keeps no pointer past the call.  Asynchronous on `stream`; host-side
+ * errors as for the runs (PA_ERR_INVALID for a NULL or misaligned pointer, a
+ * stride below Hkv*D or not a multiple of 8, missing fp8 descales).
+ */
+typedef struct {
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride_t;
+  const int32_t* cu_new;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  void* k_pool;
+  void* v_pool;
+  const float* k_descale;
+  const float* v_descale;
+} pa_append_args;
+
+pa_status pa_run_append(pa_plan_t plan, const pa_append_args* args, hipStream_t stream);
+
 /* Release a plan (NULL is ignored). */
 void pa_plan_destroy(pa_plan_t plan);
 

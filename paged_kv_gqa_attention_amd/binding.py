@@ -7,6 +7,7 @@ stream.  The functions keep the C names:
     pa_plan(desc) -> plan            pa_workspace_bytes(plan) -> int
     pa_plan_get_info(plan) -> info   pa_plan_destroy(plan)
     pa_run_prefill / pa_run_decode / pa_run_mixed(plan, args, stream) -> None
+    pa_run_append(plan, append_args, stream) -> None
     pa_status_str(code) -> str
 
 Errors are raised as ``PaError`` carrying the status code.  If libpa.so has not
@@ -31,7 +32,7 @@ PA_KV_BF16 = 0
 PA_KV_FP8_E4M3 = 1
 
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
-           "pa_run_decode", "pa_run_mixed", "pa_plan_destroy", "pa_status_str")
+           "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str")
 
 
 class PaLibraryMissing(RuntimeError):
@@ -97,6 +98,21 @@ class pa_plan_info(ctypes.Structure):
     ]
 
 
+class pa_append_args(ctypes.Structure):
+    _fields_ = [
+        ("k_new", ctypes.c_void_p),
+        ("v_new", ctypes.c_void_p),
+        ("new_stride_t", ctypes.c_int64),
+        ("cu_new", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_descale", ctypes.c_void_p),
+        ("v_descale", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -120,6 +136,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = [vp, ctypes.POINTER(pa_args), vp]
             f.restype = ctypes.c_int
+        L.pa_run_append.argtypes = [vp, ctypes.POINTER(pa_append_args), vp]
+        L.pa_run_append.restype = ctypes.c_int
         L.pa_plan_destroy.argtypes = [vp]
         L.pa_plan_destroy.restype = None
         L.pa_status_str.argtypes = [ctypes.c_int]
@@ -174,6 +192,12 @@ def pa_run_mixed(plan, args: pa_args, stream) -> None:
     _run("pa_run_mixed", plan, args, stream)
 
 
+def pa_run_append(plan, args: "pa_append_args", stream) -> None:
+    rc = lib().pa_run_append(plan, ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_run_append")
+
+
 # ---------------------------------------------------------------------------
 # torch marshalling helpers
 # ---------------------------------------------------------------------------
@@ -208,6 +232,15 @@ def make_args(*, q, k_pool, v_pool, page_table, cu_q_lens, seq_lens, softmax_sca
                    causal=1 if causal else 0, k_descale=_ptr(k_descale),
                    v_descale=_ptr(v_descale), out=_ptr(out), o_stride_t=o_stride_t,
                    lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=ws_bytes)
+
+
+def make_append_args(*, k_new, v_new, cu_new, seq_lens, page_table, k_pool, v_pool,
+                     k_descale=None, v_descale=None, new_stride_t: int = 0) -> "pa_append_args":
+    """Build pa_append_args from device tensors."""
+    return pa_append_args(k_new=_ptr(k_new), v_new=_ptr(v_new), new_stride_t=new_stride_t,
+                          cu_new=_ptr(cu_new), seq_lens=_ptr(seq_lens),
+                          page_table=_ptr(page_table), k_pool=_ptr(k_pool), v_pool=_ptr(v_pool),
+                          k_descale=_ptr(k_descale), v_descale=_ptr(v_descale))
 
 
 def current_stream() -> int:

@@ -25,6 +25,7 @@ constexpr size_t kWsAlign = 256;
 int ilog2(int64_t x) { int s = 0; while ((int64_t(1) << s) < x) ++s; return s; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -150,13 +151,49 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info) {
   return PA_OK;
 }
 
+pa_status pa_run_append(pa_plan_t plan, const pa_append_args* a, hipStream_t stream) {
+  if (!plan || !a) return PA_ERR_INVALID;
+  const pa_desc& d = plan->d;
+  if (d.num_seqs == 0) return PA_OK;
+  const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
+  const int64_t row = (int64_t)d.num_kv_heads * d.head_dim;
+  const int64_t stride = a->new_stride_t ? a->new_stride_t : row;
+  if (!a->k_new || !a->v_new || !a->cu_new || !a->seq_lens || !a->page_table || !a->k_pool || !a->v_pool)
+    return PA_ERR_INVALID;
+  if (!aligned16(a->k_new) || !aligned16(a->v_new) || !aligned16(a->k_pool) ||
+      !aligned16(a->v_pool))
+    return PA_ERR_INVALID;
+  if (stride < row || stride % 8) return PA_ERR_INVALID;
+  if (fp8 && (!a->k_descale || !a->v_descale)) return PA_ERR_INVALID;
+  pa::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.k_new = static_cast<const uint16_t*>(a->k_new);
+  p.v_new = static_cast<const uint16_t*>(a->v_new);
+  p.new_stride_t = stride;
+  p.cu_new = a->cu_new;
+  p.seq_lens = a->seq_lens;
+  p.page_table = a->page_table;
+  p.pt_row_stride = d.page_table_row_stride;
+  p.pt_cols = d.page_table_cols;
+  p.num_seqs = d.num_seqs;
+  p.num_kv_heads = d.num_kv_heads;
+  p.head_dim = d.head_dim;
+  p.page_shift = plan->page_shift;
+  p.max_new = plan->rows_cap;
+  p.kv_page_bytes = plan->kv_page_bytes;
+  p.k_pool = static_cast<uint8_t*>(a->k_pool);
+  p.v_pool = static_cast<uint8_t*>(a->v_pool);
+  p.fp8 = fp8 ? 1 : 0;
+  p.k_descale = fp8 ? a->k_descale : nullptr;
+  p.v_descale = fp8 ? a->v_descale : nullptr;
+  return pa::launch_append(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 void pa_plan_destroy(pa_plan_t plan) { delete plan; }
 
 }  // extern "C"
 
 namespace {
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Host-side checks shared by the three runs; fills the kernel parameters.
 pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_splits,

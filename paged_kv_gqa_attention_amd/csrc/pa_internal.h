@@ -62,6 +62,31 @@ struct MergeParams {
   float* lse;
 };
 
+struct AppendParams {
+  const uint16_t* k_new;        // bf16 bits [T_new, Hkv, D]
+  const uint16_t* v_new;
+  int64_t new_stride_t;         // elements between new tokens
+  const int32_t* cu_new;        // [B+1]
+  const int32_t* seq_lens;      // [B], after the append
+  const int32_t* page_table;    // [B, pt_row_stride]
+  int32_t pt_row_stride;
+  int32_t pt_cols;              // positions at or past C * page are not written
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_shift;
+  int32_t max_new;              // token rows at or past this index are not written
+  int64_t kv_page_bytes;        // bytes between physical pages
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int32_t fp8;
+  const float* k_descale;
+  const float* v_descale;
+};
+
+// Launch the KV-cache append.
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
 // Launch the attention kernel instance for (head_dim, kv dtype, mode).
 hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnParams& p,
                             dim3 grid, hipStream_t stream);

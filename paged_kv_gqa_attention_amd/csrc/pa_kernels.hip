@@ -1261,6 +1261,89 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     p.lse[row] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// KV-cache append: one thread per 8 elements of a new K or V row
+// ---------------------------------------------------------------------------
+
+// binary32 -> OCP FP8 E4M3 code: nearest value, ties to an even mantissa,
+// magnitudes at or past 448 saturate to 448 (x finite).
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, x);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __builtin_fabsf(x);
+  uint32_t code;
+  if (!(a == a)) {
+    code = 0x7Fu;                                  // NaN keeps its sign
+  } else if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    // below 2^-6: subnormal codes m * 2^-9 (m = 8 is the smallest normal);
+    // the scaling is exact and rint rounds half to even
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t ab = bits & 0x7FFFFFFFu;
+    int e = (int)(ab >> 23) - 127;                 // -6 .. 8
+    uint32_t m = (ab >> 20) & 7u;                  // top three mantissa bits
+    const uint32_t rem = ab & 0xFFFFFu;            // the 20 bits rounded away
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) {
+      m = 0u;
+      ++e;
+    }
+    code = ((uint32_t)(e + 7) << 3) | m;           // < 448 never reaches 0x7F
+  }
+  return code | sign;
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int D = p.head_dim;
+  const int cpr = D / 8;                                   // 8-element groups per row
+  const int per_head = cpr;                                // threads per (token, head) row
+  const int per_kv = p.num_kv_heads * per_head;
+  const int64_t per_token = 2 * (int64_t)per_kv;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int total = min(p.cu_new[p.num_seqs], p.max_new);
+  if (idx >= (int64_t)total * per_token) return;
+  const int t = (int)(idx / per_token);
+  int rem = (int)(idx - (int64_t)t * per_token);
+  const int kv = rem >= per_kv ? 1 : 0;                    // 0: K row, 1: V row
+  rem -= kv * per_kv;
+  const int g = rem / per_head;
+  const int c = rem - g * per_head;
+  // the sequence that owns new token t: the last b with cu_new[b] <= t
+  int lo = 0, hi = p.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.cu_new[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
+  const int n = p.cu_new[b + 1] - p.cu_new[b];
+  const int pos = p.seq_lens[b] - n + (t - p.cu_new[b]);
+  if (pos < 0 || pos >= (p.pt_cols << p.page_shift)) return;   // contract violation: write nothing
+  const int page = p.page_table[(int64_t)b * p.pt_row_stride + (pos >> p.page_shift)];
+  const int slot = pos & ((1 << p.page_shift) - 1);
+  const uint16_t* src = (kv ? p.v_new : p.k_new) + (int64_t)t * p.new_stride_t + (int64_t)g * D + c * 8;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+  uint8_t* pool = kv ? p.v_pool : p.k_pool;
+  const int64_t elem = ((int64_t)slot * p.num_kv_heads + g) * D + c * 8;   // element offset in the page
+  if (!p.fp8) {
+    uint8_t* dst = pool + (int64_t)page * p.kv_page_bytes + elem * 2;
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else {
+    const float d = *(kv ? p.v_descale : p.k_descale);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      const float x = __builtin_bit_cast(float, h << 16);
+      w[i >> 2] |= e4m3_encode(x / d) << ((i & 3) * 8);
+    }
+    uint8_t* dst = pool + (int64_t)page * p.kv_page_bytes + elem;
+    *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+  }
+}
+
 template <int D, bool FP8, int MODE>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
@@ -1353,6 +1436,14 @@ int block_rows(int head_dim, Mode mode) {
     case 256: return block_rows_d<256>(mode);
   }
   return 0;
+}
+
+hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.max_new * 2 * p.num_kv_heads * (p.head_dim / 8);
+  if (threads <= 0 || p.num_seqs <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream) {

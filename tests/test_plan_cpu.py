@@ -156,3 +156,27 @@ def test_runs_reject_bad_arguments_without_touching_the_device():
     y.cu_q_lens = None
     assert B.lib().pa_run_prefill(p, ctypes.byref(y), None) == B.PA_ERR_INVALID
     B.pa_plan_destroy(p)
+
+
+def test_append_rejects_bad_arguments_without_touching_the_device():
+    p = B.pa_plan(desc())
+    assert B.lib().pa_run_append(p, None, None) == B.PA_ERR_INVALID
+    assert B.lib().pa_run_append(None, ctypes.byref(B.pa_append_args()), None) == B.PA_ERR_INVALID
+    assert B.lib().pa_run_append(p, ctypes.byref(B.pa_append_args()), None) == B.PA_ERR_INVALID
+    good = dict(k_new=4096, v_new=8192, cu_new=12288, seq_lens=16384, page_table=20480,
+                k_pool=24576, v_pool=28672)
+    def args(**kw):
+        v = dict(good)
+        v.update(kw)
+        x = B.pa_append_args(**v)
+        return x
+    for bad in (args(k_new=4098), args(v_pool=28680), args(seq_lens=None),
+                args(new_stride_t=12), args(new_stride_t=1028)):
+        assert B.lib().pa_run_append(p, ctypes.byref(bad), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
+    p = B.pa_plan(desc(kv_dtype=B.PA_KV_FP8_E4M3))
+    assert B.lib().pa_run_append(p, ctypes.byref(args()), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
+    p = B.pa_plan(desc(num_seqs=0))                      # nothing to append: no launch
+    assert B.lib().pa_run_append(p, ctypes.byref(B.pa_append_args()), None) == B.PA_OK
+    B.pa_plan_destroy(p)
