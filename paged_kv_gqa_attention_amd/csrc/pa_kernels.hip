@@ -1262,85 +1262,116 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// KV-cache append: one thread per 8 elements of a new K or V row
+// KV-cache append: a workgroup per 16 new tokens, a thread per 8 elements
 // ---------------------------------------------------------------------------
 
-// binary32 -> OCP FP8 E4M3 code: nearest value, ties to an even mantissa,
-// magnitudes at or past 448 saturate to 448 (x finite).
-__device__ __forceinline__ uint32_t e4m3_encode(float x) {
-  const uint32_t bits = __builtin_bit_cast(uint32_t, x);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __builtin_fabsf(x);
-  uint32_t code;
-  if (!(a == a)) {
-    code = 0x7Fu;                                  // NaN keeps its sign
-  } else if (a >= 448.0f) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    // below 2^-6: subnormal codes m * 2^-9 (m = 8 is the smallest normal);
-    // the scaling is exact and rint rounds half to even
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const uint32_t ab = bits & 0x7FFFFFFFu;
-    int e = (int)(ab >> 23) - 127;                 // -6 .. 8
-    uint32_t m = (ab >> 20) & 7u;                  // top three mantissa bits
-    const uint32_t rem = ab & 0xFFFFFu;            // the 20 bits rounded away
-    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
-    if (m == 8u) {
-      m = 0u;
-      ++e;
-    }
-    code = ((uint32_t)(e + 7) << 3) | m;           // < 448 never reaches 0x7F
-  }
-  return code | sign;
-}
+constexpr int kAppendTokens = 16;     // new tokens per workgroup, at most
+__host__ __device__ inline int append_tokens_per_block(bool fp8) { return fp8 ? 4 : kAppendTokens; }
+constexpr int kAppendBatch = 4;       // 16-byte groups a thread loads before it stores
 
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  const int D = p.head_dim;
-  const int cpr = D / 8;                                   // 8-element groups per row
-  const int per_head = cpr;                                // threads per (token, head) row
-  const int per_kv = p.num_kv_heads * per_head;
-  const int64_t per_token = 2 * (int64_t)per_kv;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int total = min(p.cu_new[p.num_seqs], p.max_new);
-  if (idx >= (int64_t)total * per_token) return;
-  const int t = (int)(idx / per_token);
-  int rem = (int)(idx - (int64_t)t * per_token);
-  const int kv = rem >= per_kv ? 1 : 0;                    // 0: K row, 1: V row
-  rem -= kv * per_kv;
-  const int g = rem / per_head;
-  const int c = rem - g * per_head;
-  // the sequence that owns new token t: the last b with cu_new[b] <= t
-  int lo = 0, hi = p.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.cu_new[mid] <= t) lo = mid;
-    else hi = mid - 1;
+// 8 bf16 values (one 16-byte group) -> 8 OCP E4M3 codes of the binary32
+// quotients value / d.  Each quotient is correctly rounded (IEEE division);
+// finite ones are clamped to +-448 (saturation, infinities included) and the
+// hardware conversion rounds to nearest even.  The conversion gives every NaN
+// the code 0xFF, so NaN codes are rewritten as 0x7F with the quotient's sign
+// (a branch no lane takes unless its group holds a NaN).
+__device__ __forceinline__ u32x2 e4m3_encode8(u32x4 v, float d) {
+  float q[8];
+  bool any_nan = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t h = (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+    const float x = __builtin_bit_cast(float, h << 16) / d;
+    const bool nan = (__builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu) > 0x7F800000u;
+    any_nan |= nan;
+    q[i] = nan ? x : __builtin_amdgcn_fmed3f(x, 448.0f, -448.0f);
   }
-  const int b = lo;
-  const int n = p.cu_new[b + 1] - p.cu_new[b];
-  const int pos = p.seq_lens[b] - n + (t - p.cu_new[b]);
-  if (pos < 0 || pos >= (p.pt_cols << p.page_shift)) return;   // contract violation: write nothing
-  const int page = p.page_table[(int64_t)b * p.pt_row_stride + (pos >> p.page_shift)];
-  const int slot = pos & ((1 << p.page_shift) - 1);
-  const uint16_t* src = (kv ? p.v_new : p.k_new) + (int64_t)t * p.new_stride_t + (int64_t)g * D + c * 8;
-  const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-  uint8_t* pool = kv ? p.v_pool : p.k_pool;
-  const int64_t elem = ((int64_t)slot * p.num_kv_heads + g) * D + c * 8;   // element offset in the page
-  if (!p.fp8) {
-    uint8_t* dst = pool + (int64_t)page * p.kv_page_bytes + elem * 2;
-    *reinterpret_cast<u32x4*>(dst) = v;
-  } else {
-    const float d = *(kv ? p.v_descale : p.k_descale);
-    uint32_t w[2] = {0u, 0u};
+  u32x2 out;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * j], q[4 * j + 1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * j + 2], q[4 * j + 3], w, true);
+    out[j] = (uint32_t)w;
+  }
+  if (any_nan) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t h = (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      const float x = __builtin_bit_cast(float, h << 16);
-      w[i >> 2] |= e4m3_encode(x / d) << ((i & 3) * 8);
+      const uint32_t b = __builtin_bit_cast(uint32_t, q[i]);
+      if ((b & 0x7FFFFFFFu) > 0x7F800000u) {
+        const uint32_t sh = (i & 3) * 8;
+        out[i >> 2] = (out[i >> 2] & ~(0xFFu << sh)) | ((0x7Fu | ((b >> 24) & 0x80u)) << sh);
+      }
     }
-    uint8_t* dst = pool + (int64_t)page * p.kv_page_bytes + elem;
-    *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+  }
+  return out;
+}
+
+// One workgroup appends `tpb` (<= kAppendTokens) consecutive new tokens: 16
+// for bf16 pools, 4 for fp8 pools, whose division and encoding keep the VALU
+// busy enough that more resident waves are needed to cover the loads.  The first
+// threads resolve each token's sequence (binary search over cu_new), position
+// and page once and publish the row's byte offset in the pools through LDS;
+// then every thread moves 16-byte groups of the tokens' K and V rows, issuing
+// kAppendBatch loads before their stores so the loads overlap.
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  __shared__ int64_t row_off[kAppendTokens];     // byte offset of the row in a pool, -1 = skip
+  const int total = min(p.cu_new[p.num_seqs], p.max_new);
+  const int tpb = append_tokens_per_block(p.fp8);
+  const int t0 = blockIdx.x * tpb;
+  if (t0 >= total) return;
+  const int esz = p.fp8 ? 1 : 2;
+  if ((int)threadIdx.x < tpb) {
+    const int t = t0 + (int)threadIdx.x;
+    int64_t off = -1;
+    if (t < total) {
+      int lo = 0, hi = p.num_seqs - 1;             // last b with cu_new[b] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_new[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int n = p.cu_new[lo + 1] - p.cu_new[lo];
+      const int pos = p.seq_lens[lo] - n + (t - p.cu_new[lo]);
+      if (pos >= 0 && pos < (p.pt_cols << p.page_shift)) {
+        const int page = p.page_table[(int64_t)lo * p.pt_row_stride + (pos >> p.page_shift)];
+        const int slot = pos & ((1 << p.page_shift) - 1);
+        off = (int64_t)page * p.kv_page_bytes + (int64_t)slot * p.num_kv_heads * p.head_dim * esz;
+      }
+    }
+    row_off[threadIdx.x] = off;
+  }
+  __syncthreads();
+  const int per_kv = p.num_kv_heads * (p.head_dim / 8);      // 16-byte groups per K (or V) row
+  const int per_token = 2 * per_kv;
+  const int groups = min(tpb, total - t0) * per_token;
+  const float kd = p.fp8 ? *p.k_descale : 1.f;
+  const float vd = p.fp8 ? *p.v_descale : 1.f;
+  for (int base = threadIdx.x; base < groups; base += kAppendBatch * 256) {
+    u32x4 v[kAppendBatch];
+    int64_t dst[kAppendBatch];
+    bool is_v[kAppendBatch];
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      // every lane loads (a group past the end re-reads group 0, always valid)
+      // so that no load sits in a branch and all kAppendBatch stay in flight
+      const int e = base + u * 256;
+      const int ec = e < groups ? e : 0;
+      const int i = ec / per_token;
+      int r = ec - i * per_token;
+      is_v[u] = r >= per_kv;
+      r -= is_v[u] ? per_kv : 0;                   // group r of the row: element 8 r
+      const int64_t off = row_off[i];
+      const uint16_t* src = (is_v[u] ? p.v_new : p.k_new) + (int64_t)(t0 + i) * p.new_stride_t + r * 8;
+      v[u] = *reinterpret_cast<const u32x4*>(src);
+      dst[u] = (e < groups && off >= 0) ? off + (int64_t)r * 8 * esz : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAppendBatch; ++u) {
+      if (dst[u] < 0) continue;
+      uint8_t* pool = (is_v[u] ? p.v_pool : p.k_pool) + dst[u];
+      if (!p.fp8) *reinterpret_cast<u32x4*>(pool) = v[u];
+      else *reinterpret_cast<u32x2*>(pool) = e4m3_encode8(v[u], is_v[u] ? vd : kd);
+    }
   }
 }
 
@@ -1439,9 +1470,9 @@ int block_rows(int head_dim, Mode mode) {
 }
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.max_new * 2 * p.num_kv_heads * (p.head_dim / 8);
-  if (threads <= 0 || p.num_seqs <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (p.max_new <= 0 || p.num_seqs <= 0) return hipSuccess;
+  const int tpb = append_tokens_per_block(p.fp8);
+  const dim3 grid((unsigned)((p.max_new + tpb - 1) / tpb));
   hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }

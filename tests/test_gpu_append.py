@@ -95,7 +95,13 @@ def assert_pools_equal(x, ko, vo, what):
     kg, vg = np_bits(x.k_pool), np_bits(x.v_pool)
     nk = int(np.sum(kg != ko))
     nv = int(np.sum(vg != vo))
-    assert nk == 0 and nv == 0, "%s: %d K and %d V elements differ" % (what, nk, nv)
+    detail = []
+    for name, g, o in (("K", kg, ko), ("V", vg, vo)):
+        idx = np.flatnonzero(g.reshape(-1) != o.reshape(-1))[:6]
+        detail += ["%s[%d] gpu %#x oracle %#x" % (name, i, g.reshape(-1)[i], o.reshape(-1)[i])
+                   for i in idx]
+    assert nk == 0 and nv == 0, "%s: %d K and %d V elements differ; %s" % (
+        what, nk, nv, "; ".join(detail))
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -170,3 +176,25 @@ def test_contract_violations_and_row_cap_write_nothing():
     idx = torch.from_numpy(np.nonzero(keep)[0])
     ko, vo = oracle_append(w, k_new[idx], v_new[idx], cu_new=cu2, seq_lens=exp_L.astype(np.int32))
     assert_pools_equal(x, ko, vo, "contract violations")
+
+
+@pytest.mark.parametrize("descale", [1.0, 0.125, 0.0123, 3.7])
+def test_fp8_encoder_every_bf16_value(descale):
+    # every bf16 bit pattern (NaN payloads, infinities, subnormals, both zeros)
+    # divided by a descale and encoded, against the oracle
+    w = synth.build(name="every_bf16", seq_lens=[200, 100], q_lens=[150, 60], num_q_heads=4,
+                    num_kv_heads=2, head_dim=256, page_size=16, seed=77, kv_dtype="fp8_e4m3",
+                    threads=1)
+    w.k_descale = descale
+    w.v_descale = descale * 0.5
+    n = w.total_q * w.num_kv_heads * w.head_dim
+    assert n >= 1 << 16
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(5)
+    kb = np.concatenate([allbits, rng.integers(0, 1 << 16, n - (1 << 16)).astype(np.uint16)])
+    vb = rng.permutation(kb)
+    k_new = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).view(w.total_q, -1)
+    v_new = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).view(w.total_q, -1)
+    x, _ = gpu_append(w, k_new, v_new)
+    ko, vo = oracle_append(w, k_new, v_new)
+    assert_pools_equal(x, ko, vo, "every bf16, descale %g" % descale)
