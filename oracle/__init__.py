@@ -61,6 +61,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_double),
         ("k_descale", ctypes.c_double),
         ("v_descale", ctypes.c_double),
+        ("softcap", ctypes.c_double),
     ]
 
 
@@ -125,7 +126,7 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
               rows: Optional[Sequence[int]] = None,
               key_begin: int = 0, key_end: int = -1,
               q_stride_t: int = 0, kv_page_stride: int = 0,
-              pt_cols: Optional[int] = None, threads: int = 0):
+              pt_cols: Optional[int] = None, threads: int = 0, softcap: float = 0.0):
     """Reference attention in fp64.
 
     q_bits   : uint16 bf16 bit patterns, [T, Hq, D] (or a flat buffer with
@@ -157,7 +158,7 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                  pt_row_stride=page_table.shape[1],
                  kv_page_stride=kv_page_stride, q_stride_t=q_stride_t,
                  kv_dtype=kv_dtype, causal=1 if causal else 0, scale=scale,
-                 k_descale=k_descale, v_descale=v_descale)
+                 k_descale=k_descale, v_descale=v_descale, softcap=softcap)
     T = int(cu_q_lens[B]) if B else 0
     if rows is None:
         rows_arr = None

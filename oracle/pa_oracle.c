@@ -64,6 +64,7 @@ static int check_problem(const pao_problem* pr) {
   if (pr->num_q_heads % pr->num_kv_heads) return PAO_ERR_ARG;
   if (pr->kv_dtype != PAO_KV_BF16 && pr->kv_dtype != PAO_KV_FP8_E4M3)
     return PAO_ERR_ARG;
+  if (!(pr->softcap >= 0.0) || isinf(pr->softcap)) return PAO_ERR_ARG;
   return PAO_OK;
 }
 
@@ -131,6 +132,11 @@ static void one_row(const pao_problem* pr, const uint16_t* q,
       dot += pao_bf16_to_double(qrow[d]) *
              kv_elem(pr, k_pool, phys, slot, g, d, pr->k_descale);
     s[j - lo] = pr->scale * dot;
+    /* Logit soft-capping: the unified kernel of vLLM PR #16828 (review thread
+     * on the masked-score line) caps the scaled scores before the mask; the
+     * page names the step without its formula, read here as the usual
+     * c * tanh(s / c). */
+    if (pr->softcap > 0.0) s[j - lo] = pr->softcap * tanh(s[j - lo] / pr->softcap);
     if (s[j - lo] > m) m = s[j - lo];
   }
   double l = 0.0;

@@ -22,7 +22,8 @@
  *   visible : j < L and (causal == 0 or j <= pos), intersected with an
  *             optional key window [key_begin, key_end) used for split-KV
  *             partials
- *   s_j     : scale * sum_d q[t][h][d] * K_j[d]      (fp64)
+ *   s_j     : scale * sum_d q[t][h][d] * K_j[d]      (fp64); with a soft cap
+ *             c > 0 the score becomes c * tanh(s_j / c) before the softmax
  *   LSE     : max_j s_j + ln sum_j exp(s_j - max)    (natural log)
  *   O       : sum_j exp(s_j - LSE) * V_j             (fp64)
  *   empty visible set: O = 0 and LSE = -inf
@@ -69,6 +70,7 @@ typedef struct {
   double scale;            /* softmax scale applied to q.k */
   double k_descale;        /* fp8 only: K value = e4m3(byte) * k_descale */
   double v_descale;        /* fp8 only: V value = e4m3(byte) * v_descale */
+  double softcap;          /* > 0: scores s -> softcap * tanh(s / softcap); 0: off */
 } pao_problem;
 
 /* Exact decoders of the element formats. */

@@ -58,6 +58,7 @@ class Workload:
     k_descale: float = 1.0
     v_descale: float = 1.0
     poison_page: int = -1
+    softcap: float = 0.0         # > 0: scores s -> softcap * tanh(s / softcap)
 
     @property
     def num_seqs(self) -> int:

@@ -26,7 +26,7 @@ def bits(w: synth.Workload):
 
 
 def run_oracle(w: synth.Workload, rows=None, key_begin=0, key_end=-1, causal=None,
-               scale=None, threads=0):
+               scale=None, threads=0, softcap=None):
     q, k, v = bits(w)
     return oracle.attention(
         q_bits=q, k_pool=k, v_pool=v, page_table=w.page_table.numpy(),
@@ -36,7 +36,8 @@ def run_oracle(w: synth.Workload, rows=None, key_begin=0, key_end=-1, causal=Non
         causal=w.causal if causal is None else causal,
         kv_dtype=oracle.KV_BF16 if w.kv_dtype == "bf16" else oracle.KV_FP8_E4M3,
         k_descale=w.k_descale, v_descale=w.v_descale, rows=rows,
-        key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads)
+        key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads,
+        softcap=w.softcap if softcap is None else softcap)
 
 
 def decoded_pools(w: synth.Workload):
