@@ -94,7 +94,8 @@ def time_steps(fn, steps: int, warmup: int, stream):
     return start.elapsed_time(end) / steps       # ms per step
 
 
-def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, heads=2):
+def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, heads=2,
+                   softcap=0.0):
     """Generate, time, and (CPU leg) check sampled rows.  Returns a result dict."""
     import torch
     from paged_kv_gqa_attention_amd import binding as B
@@ -103,6 +104,7 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
 
     t0 = time.time()
     w = synth.WORKLOADS[name]()
+    w.softcap = softcap
     gen_s = time.time() - t0
     x = DeviceInputs(w)
     pa = PagedAttention(w)
@@ -120,7 +122,8 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
     qo = w.qo_bytes()
     flops = w.flops()
     res = {
-        "workload": name, "entry": "pa_run_" + mode, "ms_per_step": ms,
+        "workload": name + ("_softcap%g" % softcap if softcap else ""), "entry": "pa_run_" + mode,
+        "ms_per_step": ms, "softcap": softcap,
         "kv_bytes": kv, "qo_bytes": qo, "flops": flops,
         "kv_gbs": kv / (ms * 1e-3) / 1e9,
         "alg_gbs": (kv + qo) / (ms * 1e-3) / 1e9,
@@ -239,6 +242,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one workload by name and print it")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit soft cap for --only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -272,7 +276,8 @@ def main():
         if a.only.startswith("append_"):
             r = bench_append(a.only[len("append_"):], a.steps, a.warmup)
         else:
-            r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg)
+            r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg,
+                               softcap=a.softcap)
         print(json.dumps(strip(r)), flush=True)
         return
 
@@ -297,6 +302,15 @@ def main():
             sec[name] = e
             print("# %s validated=%s ms=%.4f frac=%.3f" % (name, r["valid"], r["ms_per_step"], frac),
                   file=sys.stderr, flush=True)
+        r = bench_workload("prefill_causal", "prefill", max(5, a.steps // 2), a.warmup, cpu_leg,
+                           softcap=30.0)
+        e = strip(r)
+        e["bound"] = "mfma"
+        e["roofline_frac"] = r["tflops"] / BF16_PEAK_TFLOPS
+        sec[r["workload"]] = e
+        print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
+                                                       e["roofline_frac"]),
+              file=sys.stderr, flush=True)
         for kv in ("bf16", "fp8_e4m3"):
             r = bench_append(kv, a.steps, a.warmup)
             sec[r["workload"]] = r

@@ -145,6 +145,11 @@ typedef struct pa_plan_s* pa_plan_t;
  *                 visible key get O = 0 and LSE = -inf.
  *   workspace     device scratch of at least pa_workspace_bytes(plan) bytes,
  *                 256-byte aligned; may be NULL when that size is 0
+ *   softcap       host float; 0 = off, > 0 = logit soft-capping: each scaled
+ *                 score s becomes softcap * tanh(s / softcap) before the mask
+ *                 and the softmax (the capped scores of the unified kernel in
+ *                 vLLM PR #16828, review thread on the masked-score line).
+ *                 Negative, NaN or infinite values give PA_ERR_INVALID.
  */
 typedef struct {
   const void* q;
@@ -163,6 +168,7 @@ typedef struct {
   float* lse;
   void* workspace;
   size_t workspace_bytes;
+  float softcap;
 } pa_args;
 
 /* What a plan chose (for tests and benchmarks). */

@@ -67,13 +67,14 @@ class PagedAttention:
 
     def args(self, x: DeviceInputs, out: torch.Tensor, lse: Optional[torch.Tensor],
              causal: Optional[bool] = None, scale: Optional[float] = None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, softcap: Optional[float] = None):
         return B.make_args(q=x.q, k_pool=x.k_pool, v_pool=x.v_pool, page_table=x.page_table,
                            cu_q_lens=x.cu_q_lens, seq_lens=x.seq_lens,
                            softmax_scale=self.w.scale if scale is None else scale,
                            causal=self.w.causal if causal is None else causal,
                            out=out, lse=lse, k_descale=x.k_descale, v_descale=x.v_descale,
-                           workspace=self.workspace if workspace is None else workspace)
+                           workspace=self.workspace if workspace is None else workspace,
+                           softcap=self.w.softcap if softcap is None else softcap)
 
     def new_outputs(self, x: DeviceInputs):
         T, Hq, D = x.q.shape

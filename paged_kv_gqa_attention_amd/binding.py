@@ -83,6 +83,7 @@ class pa_args(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("softcap", ctypes.c_float),
     ]
 
 
@@ -223,7 +224,7 @@ def make_desc(*, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: i
 
 def make_args(*, q, k_pool, v_pool, page_table, cu_q_lens, seq_lens, softmax_scale: float,
               causal: bool, out, lse=None, k_descale=None, v_descale=None, workspace=None,
-              q_stride_t: int = 0, o_stride_t: int = 0) -> pa_args:
+              q_stride_t: int = 0, o_stride_t: int = 0, softcap: float = 0.0) -> pa_args:
     """Build pa_args from device tensors (no copies, no checks beyond the C side)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return pa_args(q=_ptr(q), q_stride_t=q_stride_t, k_pool=_ptr(k_pool), v_pool=_ptr(v_pool),
@@ -231,7 +232,8 @@ def make_args(*, q, k_pool, v_pool, page_table, cu_q_lens, seq_lens, softmax_sca
                    seq_lens=_ptr(seq_lens), softmax_scale=float(softmax_scale),
                    causal=1 if causal else 0, k_descale=_ptr(k_descale),
                    v_descale=_ptr(v_descale), out=_ptr(out), o_stride_t=o_stride_t,
-                   lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=ws_bytes)
+                   lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=ws_bytes,
+                   softcap=float(softcap))
 
 
 def make_append_args(*, k_new, v_new, cu_new, seq_lens, page_table, k_pool, v_pool,

@@ -215,6 +215,7 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   if (q_stride < row || o_stride < row || q_stride % 8 || o_stride % 8) return PA_ERR_INVALID;
   // the kernels fold the scale into exp2 arguments and need it positive and finite
   if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 3.0e38f)) return PA_ERR_INVALID;
+  if (!(a->softcap >= 0.f) || !(a->softcap < 3.0e38f)) return PA_ERR_INVALID;
   const bool split = use_splits && plan->num_splits > 1;
   float* part_o = nullptr;
   float* part_lse = nullptr;
@@ -243,6 +244,7 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   p.page_shift = plan->page_shift;
   p.causal = a->causal ? 1 : 0;
   p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.softcap = a->softcap;
   p.k_descale = fp8 ? a->k_descale : nullptr;
   p.v_descale = fp8 ? a->v_descale : nullptr;
   p.out = static_cast<uint16_t*>(a->out);

@@ -36,6 +36,7 @@ struct AttnParams {
   int32_t page_shift;           // log2(page size)
   int32_t causal;
   float scale_log2;             // softmax_scale * log2(e)
+  float softcap;                // > 0: scaled scores s -> softcap * tanh(s / softcap)
   const float* k_descale;       // fp8 only (device scalar)
   const float* v_descale;
   uint16_t* out;                // bf16 bits [T, Hq, D]

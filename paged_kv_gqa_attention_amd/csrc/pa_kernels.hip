@@ -379,6 +379,28 @@ __device__ __forceinline__ void mask_tile(f32x16& s, int key0, int klim, int lan
   for (int i = 0; i < 16; ++i) s[i] = key0 + acc_key(i, lane) < klim ? s[i] : neg_inf();
 }
 
+// Logit soft-capping on raw MFMA scores.  The scaled score is r * c / log2(e)
+// (c = softmax_scale * log2(e), times k_descale for fp8); capping it to
+// cap * tanh(scaled / cap) is the same as replacing r by tanh(b r) / b with
+// b = c / (cap * log2(e)), which leaves the rest of the exp2-domain softmax
+// unchanged.  tanh(x) = 1 - 2 / (exp(2x) + 1): saturates to +-1 through
+// exp2 = inf or 0.
+struct SoftCap {
+  float k2;      // 2 b log2(e) = 2 c / cap; 0 means no capping
+  float inv_b;   // cap log2(e) / c
+  __device__ SoftCap(float cap, float c)
+      : k2(cap > 0.f ? 2.f * c / cap : 0.f), inv_b(cap > 0.f ? cap * 1.44269504088896341f / c : 0.f) {}
+  __device__ bool on() const { return k2 != 0.f; }
+};
+
+__device__ __forceinline__ void cap_tile(f32x16& s, const SoftCap& sc) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float e = __builtin_amdgcn_exp2f(s[i] * sc.k2);
+    s[i] = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f) * sc.inv_b;
+  }
+}
+
 // Growth of the row max (log2 units) tolerated before the accumulator is
 // rescaled: probabilities are exp2(score - m) with m possibly stale by up to
 // this much, i.e. at most 2^8, harmless in fp32 and bf16.  The result is exact
@@ -524,6 +546,7 @@ template <int D, bool FP8, int MODE>
 __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
+  const SoftCap sc(p.softcap, c);
   constexpr int NWB = Block<MODE, D>::waves;             // waves in the workgroup
   constexpr int NW = Gm::template DecWaves<NWB>::value;   // waves that stage K/V
   constexpr int NK = Gm::dec_keys_per_lane;
@@ -612,6 +635,10 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
         __builtin_amdgcn_wave_barrier();
         f32x16 s[NT];
         score_tiles<D, FP8, Gm::k_pitch, true, NT>(s, stage, 0, nullptr, ql, Gm::q_pitch, lane);
+        if (sc.on()) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) cap_tile(s[t], sc);
+        }
         if (key0 + STEP > kfull) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) mask_tile(s[t], key0 + kSub * t, klim, lane);
@@ -692,6 +719,7 @@ template <int D, bool FP8, int MODE>
 __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                               const PageWalk& pw, int L, int split, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
+  const SoftCap sc(p.softcap, c);
   constexpr int NTH = Block<MODE, D>::threads;
   // a loader unit: NK consecutive keys x one 16-byte chunk, one unit per thread
   constexpr int NK = (kTile * Gm::chunks) / NTH > 0 ? (kTile * Gm::chunks) / NTH : 1;
@@ -805,6 +833,10 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
           for (int t = 0; t < D / 32; ++t)
 #pragma unroll
             for (int h = 0; h < 2; ++h) va[t][h] = v_operand<FP8, Gm::v_pitch>(vl, kSub * n, t, h, lane);
+          if (sc.on()) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) cap_tile(s[ct][0], sc);
+          }
           if (k0 + kSub > wave_kfull) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) mask_tile(s[ct][0], k0, klim[ct], lane);
@@ -1019,6 +1051,7 @@ template <int D, bool FP8, int MODE>
 __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                             const PageWalk& pw, int L, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
+  const SoftCap sc(p.softcap, c);
   constexpr int NW = Block<MODE, D>::waves;
   constexpr int NB = Gm::ring_bufs;
   static_assert(NB >= 3 && NB <= 4, "ring of three or four tiles");
@@ -1103,6 +1136,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
         stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch>(st, s_cur, sn[0], kl, vl, qreg, c, lane);
         if (u + 1 < nsub) {
           const int k1 = cb + (u + 1) * kSub;
+          if (sc.on()) cap_tile(sn[0], sc);
           if (k1 + kSub > wave_kfull) mask_tile(sn[0], k1, klim, lane);
           max_update<D, 1>(st, sn, c);
         }

@@ -134,9 +134,11 @@ def test_runs_reject_bad_arguments_without_touching_the_device():
         x.softmax_scale = kw.get("scale", 0.1)
         x.q_stride_t = kw.get("q_stride_t", 0)
         x.o_stride_t = kw.get("o_stride_t", 0)
+        x.softcap = kw.get("softcap", 0.0)
         return x
     for bad in (args(q=4100), args(out=28674), args(scale=0.0), args(scale=-1.0),
-                args(scale=float("nan")), args(q_stride_t=4000), args(o_stride_t=4100)):
+                args(scale=float("nan")), args(q_stride_t=4000), args(o_stride_t=4100),
+                args(softcap=-1.0), args(softcap=float("nan")), args(softcap=float("inf"))):
         assert B.lib().pa_run_decode(p, ctypes.byref(bad), None) == B.PA_ERR_INVALID
     B.pa_plan_destroy(p)
     # fp8 without descales
