@@ -95,7 +95,7 @@ def time_steps(fn, steps: int, warmup: int, stream):
 
 
 def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, heads=2,
-                   softcap=0.0):
+                   softcap=0.0, num_splits=0):
     """Generate, time, and (CPU leg) check sampled rows.  Returns a result dict."""
     import torch
     from paged_kv_gqa_attention_amd import binding as B
@@ -107,7 +107,7 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
     w.softcap = softcap
     gen_s = time.time() - t0
     x = DeviceInputs(w)
-    pa = PagedAttention(w)
+    pa = PagedAttention(w, num_splits=num_splits)
     out, lse = pa.new_outputs(x)
     stream = torch.cuda.current_stream()
     args = pa.args(x, out, lse)
@@ -129,6 +129,7 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
         "alg_gbs": (kv + qo) / (ms * 1e-3) / 1e9,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "num_splits": int(pa.info.num_splits),
+        "balanced_workgroups": int(pa.info.balanced_workgroups),
         "validated_rows": 0, "max_abs_err_o": None, "max_abs_err_lse": None,
         "valid": None, "gen_s": round(gen_s, 2), "w": w,
     }
@@ -243,6 +244,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one workload by name and print it")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft cap for --only")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="plan num_splits for --only (0 heuristic, -1 balanced decode)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -277,7 +280,7 @@ def main():
             r = bench_append(a.only[len("append_"):], a.steps, a.warmup)
         else:
             r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg,
-                               softcap=a.softcap)
+                               softcap=a.softcap, num_splits=a.num_splits)
         print(json.dumps(strip(r)), flush=True)
         return
 

@@ -98,7 +98,16 @@ typedef enum {
  *   max_seq_len           upper bound on any seq_lens[b] (used by the split heuristic;
  *                         0 means C * page_size)
  *   kv_dtype              pa_kv_dtype
- *   num_splits            split-KV factor for decode and mixed runs; 0 = heuristic
+ *   num_splits            split-KV factor for decode and mixed runs; 0 = heuristic;
+ *                         -1 = balanced decode: pa_run_decode runs one persistent
+ *                         workgroup per resident slot, each streaming an equal
+ *                         share of all (sequence, KV head) keys, and merges
+ *                         items cut between workgroups (a task-scheduled
+ *                         decode, as the PrimTS kernels of TensorRT-LLM PR
+ *                         #17399 are described in its "Description"); mixed
+ *                         runs then use the heuristic split factor.  The
+ *                         heuristic (0) itself picks balanced decode wherever
+ *                         it would split.
  *   num_cus               compute units to plan for; 0 = query the current device
  *                         (>0 lets plans be built without a GPU)
  */
@@ -179,6 +188,7 @@ typedef struct {
   int32_t group;             /* G = Hq / Hkv */
   int32_t num_cus;           /* compute units planned for */
   int32_t mixed_q_block_tokens;  /* query tokens per work item of mixed runs */
+  int32_t balanced_workgroups;   /* > 0: balanced decode with this many workgroups */
   size_t workspace_bytes;    /* = pa_workspace_bytes(plan) */
 } pa_plan_info;
 
@@ -202,8 +212,10 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info);
  * needs no workspace. */
 pa_status pa_run_prefill(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
-/* Decode: exactly one query token per sequence (T = B).  Split-KV over the
- * plan's num_splits windows, then a log-sum-exp merge pass when splits > 1. */
+/* Decode: at most one query token per sequence (token b of sequence b when
+ * cu_q_lens is NULL).  Split-KV over the plan's num_splits windows, then a
+ * log-sum-exp merge pass when splits > 1; or, for a balanced plan
+ * (num_splits = -1), the balanced persistent schedule and its merge pass. */
 pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /* Unified mixed batch: any mix of q_len_b in one main launch.  Short rows

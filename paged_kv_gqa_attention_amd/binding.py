@@ -95,6 +95,7 @@ class pa_plan_info(ctypes.Structure):
         ("group", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("mixed_q_block_tokens", ctypes.c_int32),
+        ("balanced_workgroups", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 

@@ -41,7 +41,10 @@ struct pa_plan_s {
   int32_t num_cus;
   int32_t rows_cap;          // token rows the partial buffers are laid out for
   int64_t kv_page_bytes;
-  size_t part_o_bytes;
+  int32_t balanced_wgs;      // > 0: decode runs use the balanced persistent schedule
+  size_t part_o_bytes;       // split-KV layout: partial O, then partial LSE
+  size_t bal_part_o_bytes;   // balanced layout: partial O, partial LSE, schedule
+  size_t bal_part_lse_bytes;
   size_t ws_bytes;
 };
 
@@ -64,7 +67,7 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   if (d.num_seqs < 0 || d.num_q_heads <= 0 || d.num_kv_heads <= 0 || d.head_dim <= 0 ||
       d.page_size <= 0 || d.num_pages < 0 || d.page_table_cols < 0 ||
       d.page_table_row_stride < d.page_table_cols || d.kv_page_stride < 0 ||
-      d.max_total_q < 0 || d.max_q_len < 0 || d.max_seq_len < 0 || d.num_splits < 0 ||
+      d.max_total_q < 0 || d.max_q_len < 0 || d.max_seq_len < 0 || d.num_splits < -1 ||
       d.num_cus < 0)
     return PA_ERR_INVALID;
   if (d.num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID;
@@ -111,7 +114,7 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   // windows shorter than kMinSplitKeys keys.
   const int64_t max_len = d.max_seq_len ? d.max_seq_len : capacity;
   int splits = d.num_splits;
-  if (splits == 0) {
+  if (splits <= 0) {
     const int64_t qblocks = std::max<int64_t>(1, ceil_div(d.max_total_q, p->mixed_q_block_tokens));
     const int64_t items = std::max<int64_t>(1, std::max<int64_t>(d.num_seqs, qblocks)) * d.num_kv_heads;
     const int64_t resident = pa::workgroups_per_cu(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3, pa::kDecode);
@@ -132,6 +135,25 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
     p->part_o_bytes = 0;
     p->ws_bytes = 0;
   }
+  // Balanced decode: requested (-1), or chosen by the heuristic wherever it
+  // splits, i.e. where (sequence, KV head) items are too few to fill the
+  // device in balanced rounds.  One persistent workgroup per resident slot;
+  // its workspace layout is used by decode runs only, the split layout by
+  // mixed runs, so the workspace is the larger of the two.
+  p->balanced_wgs = 0;
+  p->bal_part_o_bytes = 0;
+  p->bal_part_lse_bytes = 0;
+  if (d.num_splits == -1 || (d.num_splits == 0 && splits > 1)) {
+    const int resident = pa::workgroups_per_cu(d.head_dim, d.kv_dtype == PA_KV_FP8_E4M3, pa::kDecode);
+    const int64_t W = (int64_t)resident * cus;
+    const size_t recs = (size_t)(2 * W) * (size_t)G;
+    p->balanced_wgs = (int32_t)W;
+    p->bal_part_o_bytes = align_up(recs * (size_t)d.head_dim * sizeof(float), kWsAlign);
+    p->bal_part_lse_bytes = align_up(recs * sizeof(float), kWsAlign);
+    const size_t bal = p->bal_part_o_bytes + p->bal_part_lse_bytes +
+                       align_up((size_t)(4 + d.num_seqs + 1) * sizeof(int32_t), kWsAlign);
+    p->ws_bytes = std::max(p->ws_bytes, bal);
+  }
   *out = p;
   return PA_OK;
 }
@@ -147,6 +169,7 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info) {
   info->mixed_q_block_tokens = plan->mixed_q_block_tokens;
   info->group = plan->group;
   info->num_cus = plan->num_cus;
+  info->balanced_workgroups = plan->balanced_wgs;
   info->workspace_bytes = plan->ws_bytes;
   return PA_OK;
 }
@@ -216,10 +239,19 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   // the kernels fold the scale into exp2 arguments and need it positive and finite
   if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 3.0e38f)) return PA_ERR_INVALID;
   if (!(a->softcap >= 0.f) || !(a->softcap < 3.0e38f)) return PA_ERR_INVALID;
+  const bool balanced = mode == pa::kDecode && plan->balanced_wgs > 0;
   const bool split = use_splits && plan->num_splits > 1;
   float* part_o = nullptr;
   float* part_lse = nullptr;
-  if (split) {
+  int32_t* sched = nullptr;
+  if (balanced && d.num_seqs > 0) {
+    if (!a->workspace || a->workspace_bytes < plan->ws_bytes) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & (kWsAlign - 1)) != 0) return PA_ERR_INVALID;
+    char* ws = static_cast<char*>(a->workspace);
+    part_o = reinterpret_cast<float*>(ws);
+    part_lse = reinterpret_cast<float*>(ws + plan->bal_part_o_bytes);
+    sched = reinterpret_cast<int32_t*>(ws + plan->bal_part_o_bytes + plan->bal_part_lse_bytes);
+  } else if (split) {
     if (!a->workspace || a->workspace_bytes < plan->ws_bytes) return PA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(a->workspace) & (kWsAlign - 1)) != 0) return PA_ERR_INVALID;
     part_o = static_cast<float*>(a->workspace);
@@ -256,12 +288,32 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   p.part_lse = part_lse;
   p.max_total_q = plan->rows_cap;
   p.q_block_tokens = mode == pa::kPrefill ? plan->q_block_tokens : plan->mixed_q_block_tokens;
+  p.balanced = balanced ? 1 : 0;
+  p.sched = sched;
   return PA_OK;
 }
 
 pa_status launch(pa_plan_t plan, const pa::AttnParams& p, pa::Mode mode, hipStream_t stream) {
   const pa_desc& d = plan->d;
   if (d.num_seqs == 0) return PA_OK;
+  const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
+  if (p.balanced) {
+    const dim3 grid((unsigned)plan->balanced_wgs, 1, 1);
+    if (pa::launch_attention(d.head_dim, fp8, mode, p, grid, stream) != hipSuccess) return PA_ERR_HIP;
+    pa::BalancedMergeParams m;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.sched = p.sched;
+    m.num_seqs = d.num_seqs;
+    m.num_q_heads = d.num_q_heads;
+    m.num_kv_heads = d.num_kv_heads;
+    m.max_total_q = p.max_total_q;
+    m.cu_q_lens = p.cu_q_lens;
+    m.out = p.out;
+    m.o_stride_t = p.o_stride_t;
+    m.lse = p.lse;
+    return pa::launch_merge_balanced(d.head_dim, m, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  }
   dim3 grid;
   if (mode == pa::kDecode) {
     grid = dim3((unsigned)d.num_seqs, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
@@ -269,7 +321,6 @@ pa_status launch(pa_plan_t plan, const pa::AttnParams& p, pa::Mode mode, hipStre
     const int64_t blocks = (int64_t)plan->rows_cap / p.q_block_tokens + d.num_seqs;
     grid = dim3((unsigned)blocks, (unsigned)d.num_kv_heads, (unsigned)p.num_splits);
   }
-  const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
   if (pa::launch_attention(d.head_dim, fp8, mode, p, grid, stream) != hipSuccess) return PA_ERR_HIP;
   if (p.num_splits > 1) {
     pa::MergeParams m;

@@ -48,6 +48,8 @@ struct AttnParams {
   float* part_lse;              // [S][max_total_q][Hq], log2 units
   int32_t max_total_q;          // rows at or past this token index are not computed
   int32_t q_block_tokens;       // tokens per q-block (prefill / mixed)
+  int32_t balanced;             // decode only: persistent balanced schedule (see launch)
+  int32_t* sched;               // balanced: [4 + B + 1] ints of workspace (unit offsets)
 };
 
 struct MergeParams {
@@ -84,6 +86,23 @@ struct AppendParams {
   const float* k_descale;
   const float* v_descale;
 };
+
+struct BalancedMergeParams {
+  const float* part_o;          // [2 W][G][D], O / l of cut pieces
+  const float* part_lse;        // [2 W][G], log2 units
+  const int32_t* sched;         // U, total, -, -, S_0 .. S_B (written by the attention kernel)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_total_q;
+  const int32_t* cu_q_lens;     // NULL: token b = sequence b
+  uint16_t* out;
+  int64_t o_stride_t;
+  float* lse;
+};
+
+// Launch the merge of balanced decode pieces.
+hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream);
 
 // Launch the KV-cache append.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

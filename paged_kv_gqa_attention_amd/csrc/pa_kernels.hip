@@ -498,7 +498,7 @@ struct RowMap {
 // already the full row sum (both lane halves).
 template <int D>
 __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float l_tot, int r0,
-                           const RowMap& rm, int split, float vdesc, int lane) {
+                           const RowMap& rm, int slot, float vdesc, int lane) {
   const int r = r0 + (lane & 31);
   const int tok = r / rm.G;
   if (tok >= rm.ntok) return;
@@ -508,8 +508,11 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
   const bool empty = !(l_tot > 0.f);
   const float inv = empty ? 0.f : vdesc / l_tot;
   const float lse2 = empty ? neg_inf() : st.m + __builtin_amdgcn_logf(l_tot);  // v_log_f32 is log2
-  if (p.num_splits > 1) {
-    const int64_t row = ((int64_t)split * p.max_total_q + t) * p.num_q_heads + h;
+  if (slot >= 0) {
+    // partial (O / l, log2 LSE): split-KV slots hold [split][token][head]
+    // records; balanced decode slots hold the G rows of one item
+    const int64_t row = p.balanced ? (int64_t)slot * rm.G + r
+                                   : ((int64_t)slot * p.max_total_q + t) * p.num_q_heads + h;
     if ((lane >> 5) == 0) p.part_lse[row] = lse2;
     if (empty) return;
     float* dst = p.part_o + row * D;
@@ -544,7 +547,8 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
 
 template <int D, bool FP8, int MODE>
 __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
-                              const PageWalk& pw, int L, int split, float c, float vdesc) {
+                              const PageWalk& pw, int L, int klo, int khi, int slot, float c,
+                              float vdesc) {
   using Gm = Geo<D, FP8>;
   const SoftCap sc(p.softcap, c);
   constexpr int NWB = Block<MODE, D>::waves;             // waves in the workgroup
@@ -554,16 +558,14 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nrows = rm.ntok * rm.G;
 
-  // key window of this split, clipped by the causal limit of the last token
-  const int klo = split * p.split_keys;
-  int khi = min(L, klo + p.split_keys);
+  // key window [klo, khi), clipped by the causal limit of the last token
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
 
   SoftmaxState<D> st[1];
   state_init(st[0]);
   if (khi <= klo) {
     // empty window: the (partial) rows are empty, nothing to stage or stream
-    if (wave == 0) write_rows<D>(p, st[0], 0.f, 0, rm, split, vdesc, lane);
+    if (wave == 0) write_rows<D>(p, st[0], 0.f, 0, rm, slot, vdesc, lane);
     return;
   }
 
@@ -707,7 +709,7 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   }
   if (wave == 0) {
     const float l_tot = st[0].l + xor32(st[0].l);
-    write_rows<D>(p, st[0], l_tot, 0, rm, split, vdesc, lane);
+    write_rows<D>(p, st[0], l_tot, 0, rm, slot, vdesc, lane);
   }
 }
 
@@ -869,7 +871,7 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const float l_tot = st[ct].l + xor32(st[ct].l);
-      write_rows<D>(p, st[ct], l_tot, r0 + ct * kCols, rm, split, vdesc, lane);
+      write_rows<D>(p, st[ct], l_tot, r0 + ct * kCols, rm, p.num_splits > 1 ? split : -1, vdesc, lane);
     }
   }
 }
@@ -1146,13 +1148,154 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   }
   if (wave_active) {
     const float l_tot = st.l + xor32(st.l);
-    write_rows<D>(p, st, l_tot, r0, rm, 0, vdesc, lane);
+    write_rows<D>(p, st, l_tot, r0, rm, -1, vdesc, lane);
   }
 }
 
 // ---------------------------------------------------------------------------
 // the kernel: work-item decode, then one of the schedules
 // ---------------------------------------------------------------------------
+
+// Row map and page walk of the item (sequence b, KV head g, query tokens
+// t0 .. t0+ntok-1 at offset i0 of its q_len); returns the live key count.
+template <int D, bool FP8>
+__device__ __forceinline__ int item_setup(const AttnParams& p, int b, int g, int t0, int ntok, int q_len,
+                                          int i0, RowMap& rm, PageWalk& pw) {
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  rm.t0 = t0;
+  rm.ntok = ntok;
+  // position of the block's first token: the queries are the last q_len keys
+  rm.pos0 = L - q_len + i0;
+  rm.g = g;
+  rm.G = p.group;
+  pw.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
+  pw.page_bytes = p.kv_page_bytes;
+  pw.head_off = (int64_t)g * Geo<D, FP8>::row_bytes;
+  pw.row_stride_b = p.num_kv_heads * Geo<D, FP8>::row_bytes;
+  pw.shift = p.page_shift;
+  pw.klimit = L;
+  return L;
+}
+
+// Exp2-domain score scale (softmax_scale * log2 e, times k_descale for fp8)
+// and the factor applied to O at the end (v_descale for fp8).
+template <bool FP8>
+__device__ __forceinline__ void score_scales(const AttnParams& p, float& c, float& vdesc) {
+  c = p.scale_log2;
+  vdesc = 1.f;
+  if (FP8) {
+    c *= *p.k_descale;
+    vdesc = *p.v_descale;
+  }
+}
+
+// Balanced (persistent) decode.  The items (sequence b, KV head g) are laid
+// end to end in units of kUnitKeys keys, b-major: item (b, g) covers units
+// [Hkv S_b + g s_b, + s_b) with s_b = ceil(L_b / kUnitKeys) (0 when the
+// sequence has no query token) and S_b the prefix sum of s.  The grid holds
+// exactly the workgroups that fit on the device at once; workgroup w takes
+// units [w U, (w+1) U), U = ceil(total / grid), and runs them piece by piece
+// (a piece = the part of one item inside the range) with the decode schedule.
+// A piece that is a whole item writes its rows; a cut piece writes a partial
+// record into slot 2w (the range's first piece) or 2w+1 (its last), and
+// merge_balanced_kernel combines the pieces of cut items.  Every workgroup
+// has the same number of keys to stream, so no tail of long items is left to
+// a few compute units.  Workgroup 0 publishes U, the total and S_b for the
+// merge in p.sched.
+constexpr int kUnitKeys = 128;
+constexpr int kUnitShift = 7;
+
+__device__ __forceinline__ int seq_units(const AttnParams& p, int b) {
+  const int qn = p.cu_q_lens ? p.cu_q_lens[b + 1] - p.cu_q_lens[b] : 1;
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  return (qn > 0 && L > 0) ? (L + kUnitKeys - 1) >> kUnitShift : 0;
+}
+
+template <int D, bool FP8, int MODE>
+__device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pcache, int* meta) {
+  constexpr int NTH = Block<MODE, D>::threads;
+  const int tid = threadIdx.x;
+  const int B = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  // units per thread chunk of sequences, then an exclusive scan over threads
+  const int per = (B + NTH - 1) / NTH;
+  const int j0 = min(B, tid * per), j1 = min(B, j0 + per);
+  int mine = 0;
+  for (int j = j0; j < j1; ++j) mine += seq_units(p, j);
+  int* scan = reinterpret_cast<int*>(smem);
+  scan[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < NTH; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = scan[tid] - mine;           // sequence units before this chunk
+  const int total = scan[NTH - 1] * Hkv;       // item units in the whole batch
+  const int W = gridDim.x;
+  const int U = (total + W - 1) / max(W, 1);
+  const int w = blockIdx.x;
+  const int u0 = min(total, w * U);
+  const int u1 = min(total, u0 + U);
+  if (w == 0) {
+    if (tid == 0) {
+      p.sched[0] = U;
+      p.sched[1] = total;
+    }
+    int acc = excl;
+    for (int j = j0; j < j1; ++j) {
+      p.sched[4 + j] = acc;
+      acc += seq_units(p, j);
+    }
+    if (tid == NTH - 1) p.sched[4 + B] = acc;
+  }
+  // the sequence holding unit u0
+  if (u0 < u1 && Hkv * excl <= u0 && u0 < Hkv * (excl + mine)) {
+    int acc = excl;
+    for (int j = j0; j < j1; ++j) {
+      const int sj = seq_units(p, j);
+      if (u0 < Hkv * (acc + sj)) {
+        meta[0] = j;
+        meta[1] = acc;
+        break;
+      }
+      acc += sj;
+    }
+  }
+  __syncthreads();
+  if (u0 >= u1) return;
+  int b = __builtin_amdgcn_readfirstlane(meta[0]);
+  int S = __builtin_amdgcn_readfirstlane(meta[1]);
+  float c, vdesc;
+  score_scales<FP8>(p, c, vdesc);
+  int u = u0;
+  int piece = 0;
+  while (u < u1) {
+    const int sb = seq_units(p, b);
+    const int item0 = Hkv * S;
+    if (sb == 0 || u >= item0 + Hkv * sb) {     // past this sequence's items
+      S += sb;
+      ++b;
+      continue;
+    }
+    const int g = (u - item0) / sb;
+    const int a0 = item0 + g * sb;
+    const int a1 = a0 + sb;
+    const int pu1 = min(u1, a1);
+    const int t0 = p.cu_q_lens ? p.cu_q_lens[b] : b;
+    RowMap rm;
+    PageWalk pw;
+    const int L = item_setup<D, FP8>(p, b, g, t0, 1, 1, 0, rm, pw);
+    const int klo = (u - a0) << kUnitShift;
+    const int khi = min(L, (pu1 - a0) << kUnitShift);
+    const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
+    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
+    __syncthreads();                            // LDS is reused by the next piece
+    u = pu1;
+    ++piece;
+  }
+}
 
 template <int D, bool FP8, int MODE>
 __global__ __launch_bounds__((Block<MODE, D>::threads))
@@ -1161,6 +1304,12 @@ void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
+  if constexpr (MODE == kDecode) {
+    if (p.balanced) {
+      balanced_decode<D, FP8, MODE>(p, smem, pcache, meta);
+      return;
+    }
+  }
   const int split = blockIdx.z;
   int g = blockIdx.y;
   int b, t0, ntok, q_len, i0 = 0;
@@ -1216,29 +1365,16 @@ void attn_kernel(AttnParams p) {
     // no query row in this block; nothing to write
     return;
   }
-  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
   RowMap rm;
-  rm.t0 = t0;
-  rm.ntok = ntok;
-  // position of the block's first token: the queries are the last q_len keys
-  rm.pos0 = L - q_len + i0;
-  rm.g = g;
-  rm.G = p.group;
   PageWalk pw;
-  pw.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
-  pw.page_bytes = p.kv_page_bytes;
-  pw.head_off = (int64_t)g * Geo<D, FP8>::row_bytes;
-  pw.row_stride_b = p.num_kv_heads * Geo<D, FP8>::row_bytes;
-  pw.shift = p.page_shift;
-  pw.klimit = L;
-  float c = p.scale_log2;
-  float vdesc = 1.f;
-  if (FP8) {
-    c *= *p.k_descale;
-    vdesc = *p.v_descale;
-  }
+  const int L = item_setup<D, FP8>(p, b, g, t0, ntok, q_len, i0, rm, pw);
+  float c, vdesc;
+  score_scales<FP8>(p, c, vdesc);
+  const int klo = split * p.split_keys;
+  const int khi = min(L, klo + p.split_keys);
+  const int slot = p.num_splits > 1 ? split : -1;
   if constexpr (MODE == kDecode) {
-    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
+    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
     if constexpr (Block<MODE, D>::stream)
       stream_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, c, vdesc);
@@ -1246,7 +1382,7 @@ void attn_kernel(AttnParams p) {
       rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
     if (q_len * p.group <= kCols)
-      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
+      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
     else
       rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, split, c, vdesc);
   }
@@ -1293,6 +1429,67 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
   if (p.lse && lane == 0)
     p.lse[row] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+}
+
+// Rows of balanced decode whose item was cut between workgroups: combine the
+// pieces' partial records (slot rule of balanced_decode); rows of sequences
+// without keys get O = 0 and LSE = -inf; whole items were written already.
+template <int D>
+__global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedMergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // b * Hq + h
+  if (row >= (int64_t)p.num_seqs * p.num_q_heads) return;
+  const int b = (int)(row / p.num_q_heads);
+  const int h = (int)(row - (int64_t)b * p.num_q_heads);
+  const int qn = p.cu_q_lens ? p.cu_q_lens[b + 1] - p.cu_q_lens[b] : 1;
+  if (qn <= 0) return;
+  const int t = p.cu_q_lens ? p.cu_q_lens[b] : b;
+  if (t >= p.max_total_q) return;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int g = h / G, r = h - g * G;
+  const int U = p.sched[0];
+  const int S = p.sched[4 + b];
+  const int sb = p.sched[4 + b + 1] - S;
+  constexpr int PER = D / 64;     // d values per lane
+  uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + lane * PER;
+  if (sb == 0) {                  // no visible key
+#pragma unroll
+    for (int k = 0; k < PER; ++k) dst[k] = 0;
+    if (p.lse && lane == 0) p.lse[(int64_t)t * p.num_q_heads + h] = neg_inf();
+    return;
+  }
+  const int a0 = p.num_kv_heads * S + g * sb;
+  const int w0 = a0 / U, w1 = (a0 + sb - 1) / U;
+  if (w0 == w1) return;
+  float mx = neg_inf();
+  for (int wg = w0; wg <= w1; ++wg) {
+    const int slot = 2 * wg + ((wg == w0 && a0 != w0 * U) ? 1 : 0);
+    mx = fmaxf(mx, p.part_lse[(int64_t)slot * G + r]);
+  }
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float wsum = 0.f;
+  if (mx != neg_inf()) {
+    for (int wg = w0; wg <= w1; ++wg) {
+      const int64_t rec = (int64_t)(2 * wg + ((wg == w0 && a0 != w0 * U) ? 1 : 0)) * G + r;
+      const float ls = p.part_lse[rec];
+      if (ls == neg_inf()) continue;
+      const float wt = __builtin_amdgcn_exp2f(ls - mx);
+      wsum += wt;
+      const float* src = p.part_o + rec * D + lane * PER;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += wt * src[k];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const __bf16 v = (__bf16)(acc[k] * inv);
+    dst[k] = __builtin_bit_cast(uint16_t, v);
+  }
+  if (p.lse && lane == 0)
+    p.lse[(int64_t)t * p.num_q_heads + h] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -1508,6 +1705,19 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   const int tpb = append_tokens_per_block(p.fp8);
   const dim3 grid((unsigned)((p.max_new + tpb - 1) / tpb));
   hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (grid.x == 0) return hipSuccess;
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(merge_balanced_kernel<64>, grid, dim3(256), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(merge_balanced_kernel<128>, grid, dim3(256), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(merge_balanced_kernel<256>, grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -95,11 +95,25 @@ def test_split_heuristic_and_workspace():
     rows = S * 64 * 64
     assert B.pa_workspace_bytes(p) >= rows * 256 * 4 + rows * 4
     assert info.workspace_bytes == B.pa_workspace_bytes(p)
+    # where it splits, the heuristic also runs decode balanced: one workgroup per
+    # resident slot (one per CU at fp8 D 256), two partial records of G rows each
+    W = info.balanced_workgroups
+    assert W == 256
+    assert B.pa_workspace_bytes(p) >= 2 * W * 32 * (256 + 1) * 4 + (4 + 64 + 1) * 4
     B.pa_plan_destroy(p)
-    # many items: no split, no workspace
+    # many items: no split, no balanced decode, no workspace
     p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048))
-    assert B.pa_plan_get_info(p).num_splits == 1 and B.pa_workspace_bytes(p) == 0
+    info = B.pa_plan_get_info(p)
+    assert info.num_splits == 1 and info.balanced_workgroups == 0 and B.pa_workspace_bytes(p) == 0
     B.pa_plan_destroy(p)
+    # balanced decode on request; below -1 is invalid
+    p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048,
+                       num_splits=-1))
+    info = B.pa_plan_get_info(p)
+    assert info.balanced_workgroups == 2 * 256 and info.num_splits == 1
+    assert B.pa_workspace_bytes(p) >= 2 * 512 * 4 * (128 + 1) * 4
+    B.pa_plan_destroy(p)
+    assert plan_status(num_splits=-2) == B.PA_ERR_INVALID
     # forced splits are honoured (rounded to whole 128-key windows)
     p = B.pa_plan(desc(num_splits=3, page_table_cols=64, max_seq_len=1024))
     info = B.pa_plan_get_info(p)
