@@ -65,6 +65,23 @@ class Problem(ctypes.Structure):
     ]
 
 
+class MlaProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("pt_cols", ctypes.c_int32),
+        ("pt_row_stride", ctypes.c_int32),
+        ("kv_page_stride", ctypes.c_int64),
+        ("q_stride_t", ctypes.c_int64),
+        ("scale", ctypes.c_double),
+        ("softcap", ctypes.c_double),
+    ]
+
+
 _lib = None
 
 
@@ -87,6 +104,9 @@ def load(path: str):
     L.pao_fp8_e4m3_encode.restype = ctypes.c_uint8
     L.pao_append.argtypes = [ctypes.POINTER(Problem), vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp]
     L.pao_append.restype = ctypes.c_int
+    L.pao_mla_decode.argtypes = [ctypes.POINTER(MlaProblem), vp, vp, vp, vp, vp, ctypes.c_int64,
+                                 vp, vp, ctypes.c_int]
+    L.pao_mla_decode.restype = ctypes.c_int
     return L
 
 
@@ -230,3 +250,45 @@ def append(*, k_new: np.ndarray, v_new: np.ndarray, k_pool: np.ndarray, v_pool: 
     if rc != 0:
         raise OracleError("pao_append failed with code %d" % rc)
     return k_out, v_out
+
+
+def mla_decode(*, q_bits: np.ndarray, kv_cache: np.ndarray, page_table: np.ndarray,
+               seq_lens: np.ndarray, num_q_heads: int, page_size: int, scale: float,
+               d_latent: int = 512, d_rope: int = 64, softcap: float = 0.0,
+               rows: Optional[Sequence[int]] = None, q_stride_t: int = 0,
+               kv_page_stride: int = 0, pt_cols: Optional[int] = None, threads: int = 0):
+    """MLA decode in fp64 (see pa_oracle.h).
+
+    q_bits   : uint16 bf16 bits [B, Hq, d_latent + d_rope]
+    kv_cache : uint16 bf16 bits [P, page, d_latent + d_rope]
+    Returns (out, lse): [B, Hq, d_latent] and [B, Hq] when rows is None, else
+    [len(rows), d_latent] and [len(rows)] for flat rows b*Hq + h.
+    """
+    page_table = _c(page_table, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    q_bits = _c(q_bits, np.uint16)
+    kv_cache = _c(kv_cache, np.uint16)
+    B = seq_lens.shape[0]
+    Dk = d_latent + d_rope
+    per_page = kv_page_stride if kv_page_stride else page_size * Dk
+    pr = MlaProblem(num_seqs=B, num_q_heads=num_q_heads, d_latent=d_latent, d_rope=d_rope,
+                    page_size=page_size, num_pages=kv_cache.size // per_page,
+                    pt_cols=page_table.shape[1] if pt_cols is None else pt_cols,
+                    pt_row_stride=page_table.shape[1], kv_page_stride=kv_page_stride,
+                    q_stride_t=q_stride_t, scale=scale, softcap=softcap)
+    if rows is None:
+        rows_arr = None
+        n = B * num_q_heads
+    else:
+        rows_arr = _c(np.asarray(rows), np.int64)
+        n = rows_arr.shape[0]
+    out = np.zeros((n, d_latent), np.float64)
+    lse = np.zeros(n, np.float64)
+    rc = lib().pao_mla_decode(ctypes.byref(pr), _ptr(q_bits), _ptr(kv_cache), _ptr(page_table),
+                              _ptr(seq_lens), _ptr(rows_arr), int(n), _ptr(out), _ptr(lse),
+                              int(threads))
+    if rc != 0:
+        raise OracleError("pao_mla_decode failed with code %d" % rc)
+    if rows is None:
+        return out.reshape(B, num_q_heads, d_latent), lse.reshape(B, num_q_heads)
+    return out, lse

@@ -306,3 +306,95 @@ int pao_append(const pao_problem* pr, const uint16_t* k_new, const uint16_t* v_n
   }
   return PAO_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* MLA decode                                                                */
+/* ------------------------------------------------------------------------ */
+
+static void mla_row(const pao_mla_problem* pr, const uint16_t* q, const uint16_t* kv,
+                    const int32_t* page_table, const int32_t* seq_lens, int64_t row,
+                    double* s, double* o_row, double* lse_out) {
+  const int64_t Dk = (int64_t)pr->d_latent + pr->d_rope;
+  const int64_t Dv = pr->d_latent;
+  const int64_t page_stride = pr->kv_page_stride ? pr->kv_page_stride : (int64_t)pr->page_size * Dk;
+  const int64_t q_stride = pr->q_stride_t ? pr->q_stride_t : (int64_t)pr->num_q_heads * Dk;
+  const int64_t b = row / pr->num_q_heads;
+  const int64_t h = row % pr->num_q_heads;
+  const int64_t L = seq_lens[b];
+  for (int64_t d = 0; d < Dv; ++d) o_row[d] = 0.0;
+  if (L <= 0) {
+    *lse_out = -INFINITY;
+    return;
+  }
+  const uint16_t* qrow = q + b * q_stride + h * Dk;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < L; ++j) {
+    const uint16_t* c = kv + (int64_t)page_table[b * pr->pt_row_stride + j / pr->page_size] * page_stride +
+                        (j % pr->page_size) * Dk;
+    double dot = 0.0;
+    for (int64_t d = 0; d < Dk; ++d) dot += pao_bf16_to_double(qrow[d]) * pao_bf16_to_double(c[d]);
+    s[j] = pr->scale * dot;
+    if (pr->softcap > 0.0) s[j] = pr->softcap * tanh(s[j] / pr->softcap);
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < L; ++j) l += exp(s[j] - m);
+  const double lse = m + log(l);
+  for (int64_t j = 0; j < L; ++j) {
+    const uint16_t* c = kv + (int64_t)page_table[b * pr->pt_row_stride + j / pr->page_size] * page_stride +
+                        (j % pr->page_size) * Dk;
+    const double p = exp(s[j] - lse);
+    for (int64_t d = 0; d < Dv; ++d) o_row[d] += p * pao_bf16_to_double(c[d]);
+  }
+  *lse_out = lse;
+}
+
+int pao_mla_decode(const pao_mla_problem* pr, const uint16_t* q, const uint16_t* kv,
+                   const int32_t* page_table, const int32_t* seq_lens,
+                   const int64_t* rows, int64_t num_rows, double* out, double* lse,
+                   int threads) {
+  if (!pr || !q || !kv || !page_table || !seq_lens || !out) return PAO_ERR_ARG;
+  if (pr->num_seqs < 0 || pr->num_q_heads <= 0 || pr->d_latent <= 0 || pr->d_rope < 0 ||
+      pr->page_size <= 0 || pr->num_pages < 0 || pr->pt_cols < 0 ||
+      pr->pt_row_stride < pr->pt_cols || !(pr->softcap >= 0.0) || isinf(pr->softcap))
+    return PAO_ERR_ARG;
+  int64_t max_L = 0;
+  for (int32_t b = 0; b < pr->num_seqs; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 0 || L > (int64_t)pr->pt_cols * pr->page_size) return PAO_ERR_DATA;
+    for (int64_t p = 0; p < (L + pr->page_size - 1) / pr->page_size; ++p) {
+      const int32_t phys = page_table[(int64_t)b * pr->pt_row_stride + p];
+      if (phys < 0 || phys >= pr->num_pages) return PAO_ERR_DATA;
+    }
+    if (L > max_L) max_L = L;
+  }
+  const int64_t total = (int64_t)pr->num_seqs * pr->num_q_heads;
+  const int64_t n = rows ? num_rows : total;
+  if (rows)
+    for (int64_t r = 0; r < n; ++r)
+      if (rows[r] < 0 || rows[r] >= total) return PAO_ERR_DATA;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#else
+  (void)threads;
+#endif
+  int failed = 0;
+#pragma omp parallel num_threads(threads)
+  {
+    double* s = (double*)malloc((size_t)(max_L > 0 ? max_L : 1) * sizeof(double));
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < n; ++r) {
+        double l;
+        mla_row(pr, q, kv, page_table, seq_lens, rows ? rows[r] : r, s,
+                out + r * pr->d_latent, &l);
+        if (lse) lse[r] = l;
+      }
+      free(s);
+    }
+  }
+  return failed ? PAO_ERR_ARG : PAO_OK;
+}

@@ -116,7 +116,7 @@ int pao_merge(int32_t num_parts, int64_t n, int32_t head_dim,
 
 /*
  * Nearest finite OCP FP8 E4M3 code to x (ties to an even mantissa),
- * saturating to +-448.  x must not be NaN.
+ * saturating to +-448; NaN gives the NaN code with x's sign.
  */
 uint8_t pao_fp8_e4m3_encode(double x);
 
@@ -134,6 +134,43 @@ uint8_t pao_fp8_e4m3_encode(double x);
 int pao_append(const pao_problem* pr, const uint16_t* k_new, const uint16_t* v_new,
                int64_t new_stride_t, const int32_t* page_table, const int32_t* cu_new,
                const int32_t* seq_lens, void* k_pool, void* v_pool);
+
+/*
+ * MLA decode (DeepSeek-style multi-head latent attention over a paged latent
+ * cache): one logical KV head whose cached row holds the compressed latent
+ * (d_latent values) followed by the RoPE key (d_rope values).  For query head h
+ * of sequence b (one query token per sequence, row b*Hq + h):
+ *   s_j = scale * sum_{d < d_latent + d_rope} q[b][h][d] * C_j[d]   (j < L_b)
+ *   LSE = max_j s_j + ln sum_j exp(s_j - max),   O = sum_j exp(s_j - LSE) C_j[0:d_latent)
+ * i.e. the latent part of the cached row is both a key and the value.  The
+ * query holds the absorbed latent query then its RoPE part.  C_j is the row of
+ * page page_table[b][j / page], slot j % page.  Rows of a sequence with no key
+ * give O = 0, LSE = -inf.  (BF16 MLA decode with one logical KV head, at most
+ * 128 query heads, KV-LoRA rank 512 and RoPE dimension 64: TensorRT-LLM PR
+ * #17399, "Integration and supported scope".)
+ *   q     : bf16 bits, [B][q_stride_t] with head h at h*(d_latent+d_rope)
+ *   kv    : bf16 bits, [P][page][d_latent+d_rope] with kv_page_stride between pages
+ *   out   : fp64 [rows][d_latent];  lse : fp64 [rows] (may be NULL)
+ */
+typedef struct {
+  int32_t num_seqs;        /* B */
+  int32_t num_q_heads;     /* Hq */
+  int32_t d_latent;        /* KV-LoRA rank (value width) */
+  int32_t d_rope;          /* RoPE key width */
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t pt_cols;
+  int32_t pt_row_stride;
+  int64_t kv_page_stride;  /* elements between pages; 0 = page*(d_latent+d_rope) */
+  int64_t q_stride_t;      /* elements between sequences' query rows; 0 = Hq*(d_latent+d_rope) */
+  double scale;
+  double softcap;          /* > 0: s -> softcap * tanh(s / softcap); 0: off */
+} pao_mla_problem;
+
+int pao_mla_decode(const pao_mla_problem* pr, const uint16_t* q, const uint16_t* kv,
+                   const int32_t* page_table, const int32_t* seq_lens,
+                   const int64_t* rows, int64_t num_rows, double* out, double* lse,
+                   int threads);
 
 #ifdef __cplusplus
 }

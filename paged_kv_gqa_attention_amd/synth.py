@@ -299,12 +299,117 @@ def decode_fp8_long(seed: int = 5, **kw) -> Workload:
                  kv_dtype="fp8_e4m3", **kw)
 
 
+# ---------------------------------------------------------------------------
+# MLA decode workloads (DeepSeek-style latent cache: one logical KV head, a
+# 576-wide cached row = 512 latent values then 64 RoPE key values; the latent
+# part is also the value).  The measured MLA run of TensorRT-LLM PR #17399
+# (results table: DeepSeek-V3-Lite, page size 32, 1024-token inputs and
+# outputs, concurrency 64) fixes B = 64 decode rows, page 32 and lengths from
+# 1025 to 2048; its head count is not given, so both ends of the supported
+# range are built: 16 query heads (a Lite-sized model) and 128 (the maximum).
+# ---------------------------------------------------------------------------
+
+MLA_LATENT = 512
+MLA_ROPE = 64
+
+
+@dataclasses.dataclass
+class MlaWorkload:
+    name: str
+    num_q_heads: int
+    page_size: int
+    scale: float
+    q: torch.Tensor            # bf16 [B, Hq, 576]
+    kv: torch.Tensor           # bf16 [P, page, 576]
+    page_table: torch.Tensor   # int32 [B, row_stride]
+    pt_cols: int
+    seq_lens: torch.Tensor     # int32 [B]
+    poison_page: int = -1
+    softcap: float = 0.0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.numel())
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.num_seqs else 0
+
+    def kv_bytes(self) -> int:
+        """Cached bytes read once: every live row, 576 bf16 values."""
+        return int(self.seq_lens.to(torch.int64).sum()) * (MLA_LATENT + MLA_ROPE) * 2
+
+    def qo_bytes(self) -> int:
+        return self.num_seqs * self.num_q_heads * (MLA_LATENT + MLA_ROPE + MLA_LATENT) * 2
+
+    def flops(self) -> int:
+        """2 (576 + 512) flops per (query head, key) pair."""
+        return int(self.seq_lens.to(torch.int64).sum()) * self.num_q_heads * 2 * (
+            MLA_LATENT + MLA_ROPE + MLA_LATENT)
+
+
+def build_mla(*, name: str, seq_lens: Sequence[int], num_q_heads: int, page_size: int, seed: int,
+              scale: Optional[float] = None, pt_cols: Optional[int] = None,
+              pt_row_stride: Optional[int] = None, poison: bool = True,
+              threads: int = 8) -> MlaWorkload:
+    """Latent cache and queries with the same page handling as build():
+    seeded page permutation, a poison page for unused columns, NaN in dead slots."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    B, page, Dk = L.size, page_size, MLA_LATENT + MLA_ROPE
+    pages_per_seq = (L + page - 1) // page
+    need = int(pages_per_seq.sum())
+    if pt_cols is None:
+        pt_cols = int(max(1, pages_per_seq.max() if B else 1))
+    row_stride = pt_row_stride if pt_row_stride is not None else pt_cols
+    P = need + 1
+    perm = permutation(P, seed, 1)
+    pt = np.empty((B, row_stride), dtype=np.int32)
+    poison_page = int(perm[need])
+    pt[:, :] = poison_page
+    cursor = 0
+    live = np.zeros((P, page), dtype=bool)
+    for b in range(B):
+        n = int(pages_per_seq[b])
+        pt[b, :n] = perm[cursor:cursor + n]
+        cursor += n
+        for p in range(n):
+            live[pt[b, p], :min(page, int(L[b]) - p * page)] = True
+    q = normal_bf16(B * num_q_heads * Dk, seed, 2, threads).view(B, num_q_heads, Dk)
+    kv = normal_bf16(P * page * Dk, seed, 3, threads).view(P, page, Dk)
+    if poison:
+        kv[~torch.from_numpy(live)] = torch.tensor(BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16)
+    return MlaWorkload(name=name, num_q_heads=num_q_heads, page_size=page,
+                       scale=float(scale if scale is not None else 1.0 / math.sqrt(Dk)),
+                       q=q, kv=kv, page_table=torch.from_numpy(pt), pt_cols=int(pt_cols),
+                       seq_lens=torch.from_numpy(L.astype(np.int32)), poison_page=poison_page)
+
+
+def mla_decode_h16(seed: int = 6, **kw) -> MlaWorkload:
+    """B=64 MLA decode rows, 16 query heads, page 32, L ~ U[1025, 2048]."""
+    L = uniform_int(1025, 2048, 64, seed, 0)
+    return build_mla(name="mla_decode_h16", seq_lens=L, num_q_heads=16, page_size=32, seed=seed,
+                     pt_cols=64, **kw)
+
+
+def mla_decode_h128(seed: int = 7, **kw) -> MlaWorkload:
+    """B=64 MLA decode rows, 128 query heads, page 32, L ~ U[1025, 2048]."""
+    L = uniform_int(1025, 2048, 64, seed, 0)
+    return build_mla(name="mla_decode_h128", seq_lens=L, num_q_heads=128, page_size=32, seed=seed,
+                     pt_cols=64, **kw)
+
+
 WORKLOADS = {
     "tiny_mixed": tiny_mixed,
     "decode_llama8b": decode_llama8b,
     "prefill_causal": prefill_causal,
     "mixed_24b": mixed_24b,
     "decode_fp8_long": decode_fp8_long,
+    "mla_decode_h16": mla_decode_h16,
+    "mla_decode_h128": mla_decode_h128,
 }
 
 
