@@ -18,7 +18,8 @@ MUTANTS = {
                           "if (pr->causal && pos + 2 < hi) hi = pos + 2;"),
     "top_left_causal": ("const int64_t pos = L - q_len + i;", "const int64_t pos = i;"),
     "head_map_modulo": ("const int64_t g = h / G;", "const int64_t g = h % pr->num_kv_heads;"),
-    "lse_sign": ("const double lse = m + log(l);", "const double lse = m - log(l);"),
+    "lse_sign": ("l += exp(s[j - lo] - m);\n  const double lse = m + log(l);",
+                 "l += exp(s[j - lo] - m);\n  const double lse = m - log(l);"),
     "scale_dropped": ("s[j - lo] = pr->scale * dot;", "s[j - lo] = dot;"),
     "slot_shift": ("const int64_t slot = j % pr->page_size;\n    double dot",
                    "const int64_t slot = (j + 1) % pr->page_size;\n    double dot"),
