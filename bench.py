@@ -198,9 +198,61 @@ def bench_append(kv_dtype, steps, warmup):
             "bound": "hbm", "roofline_frac": gbs / HBM_PEAK_GBS, "valid": ok}
 
 
+def bench_mla(name, steps, warmup, cpu_leg, num_splits=0):
+    """pa_run_mla_decode over a latent-cache workload.  Algorithmic bytes: every
+    live 576-wide bf16 row once, plus Q and O; flops 2 (576 + 512) per (query
+    head, key)."""
+    import torch
+    from paged_kv_gqa_attention_amd import binding as B
+    from paged_kv_gqa_attention_amd import synth
+    from paged_kv_gqa_attention_amd.attention import MlaDecode
+
+    w = synth.WORKLOADS[name]()
+    m = MlaDecode(w, num_splits=num_splits)
+    out, lse = m.new_outputs()
+    a = m.args(out, lse)
+    stream = torch.cuda.current_stream()
+    s_ptr = int(stream.cuda_stream)
+
+    def step():
+        B.pa_run_mla_decode(m.plan, a, s_ptr)
+
+    ms = time_steps(step, steps, warmup, stream)
+    kv, qo, flops = w.kv_bytes(), w.qo_bytes(), w.flops()
+    gbs = (kv + qo) / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": name, "entry": "pa_run_mla_decode", "ms_per_step": ms,
+           "num_q_heads": w.num_q_heads, "num_splits": m.num_splits, "kv_bytes": kv,
+           "qo_bytes": qo, "flops": flops, "alg_gbs": gbs, "tflops": tf, "bound": "hbm",
+           "roofline_frac": max(gbs / HBM_PEAK_GBS, tf / BF16_PEAK_TFLOPS),
+           "valid": None, "max_abs_err_o": None, "max_abs_err_lse": None}
+    if cpu_leg:
+        res.update(oracle_check_mla(w, out, lse))
+    return res
+
+
 # ---------------------------------------------------------------------------
 # CPU leg: the only code here that runs the oracle
 # ---------------------------------------------------------------------------
+
+def oracle_check_mla(w, out, lse, n=96):
+    """Sampled (sequence, head) rows of an MLA run against the fp64 oracle."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(5)
+    rows = sorted(set(int(b) * w.num_q_heads + int(h) for b, h in
+                      zip(rng.integers(0, w.num_seqs, n), rng.integers(0, w.num_q_heads, n))))
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    ro, rl = oracle.mla_decode(q_bits=bits(w.q), kv_cache=bits(w.kv),
+                               page_table=w.page_table.numpy(), seq_lens=w.seq_lens.numpy(),
+                               num_q_heads=w.num_q_heads, page_size=w.page_size, scale=w.scale,
+                               rows=rows, pt_cols=w.pt_cols, softcap=w.softcap)
+    o = out.float().cpu().numpy().reshape(-1, 512)[rows].astype(np.float64)
+    l = lse.float().cpu().numpy().reshape(-1)[rows].astype(np.float64)
+    eo = float(np.max(np.abs(o - ro)))
+    el = float(np.max(np.abs(l - rl)))
+    return {"valid": bool(np.all(np.isfinite(o)) and eo <= O_TOL["bf16"] and el <= LSE_TOL),
+            "max_abs_err_o": eo, "max_abs_err_lse": el, "validated_rows": len(rows)}
 
 def oracle_check(w, out, lse, rows):
     """Compare sampled output rows with the fp64 oracle's."""
@@ -278,6 +330,8 @@ def main():
     if a.only:
         if a.only.startswith("append_"):
             r = bench_append(a.only[len("append_"):], a.steps, a.warmup)
+        elif a.only.startswith("mla_"):
+            r = bench_mla(a.only, a.steps, a.warmup, cpu_leg, num_splits=a.num_splits)
         else:
             r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg,
                                softcap=a.softcap, num_splits=a.num_splits)
@@ -314,6 +368,12 @@ def main():
         print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
                                                        e["roofline_frac"]),
               file=sys.stderr, flush=True)
+        for name in ("mla_decode_h16", "mla_decode_h128"):
+            r = bench_mla(name, a.steps, a.warmup, cpu_leg)
+            sec[name] = r
+            print("# %s validated=%s ms=%.4f frac=%.3f" % (name, r["valid"], r["ms_per_step"],
+                                                           r["roofline_frac"]),
+                  file=sys.stderr, flush=True)
         for kv in ("bf16", "fp8_e4m3"):
             r = bench_append(kv, a.steps, a.warmup)
             sec[r["workload"]] = r

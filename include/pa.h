@@ -269,6 +269,85 @@ pa_status pa_run_append(pa_plan_t plan, const pa_append_args* args, hipStream_t 
 /* Release a plan (NULL is ignored). */
 void pa_plan_destroy(pa_plan_t plan);
 
+/*
+ * MLA decode (DeepSeek-style multi-head latent attention), the third path of
+ * TensorRT-LLM PR #17399 ("Integration and supported scope": BF16 MLA decode,
+ * one logical KV head, at most 128 local query heads, KV-LoRA rank 512, RoPE
+ * head dimension 64; "Planning, preprocessing, and workspace ownership": MLA
+ * sizes only its own scratch).  Each cached token is one 576-wide bf16 row:
+ * the 512 compressed latent values, then the 64-wide RoPE key.  For query head
+ * h of sequence b (one query token per sequence):
+ *   s_j = softmax_scale * q[b][h] . C_j  over all 576 columns, j < seq_lens[b]
+ *   (optionally soft-capped), out[b][h] = sum_j softmax_j * C_j[0:512],
+ *   lse[b][h] = ln sum_j exp(s_j)
+ * i.e. the latent part of the row is both key and value.  Same page-table and
+ * seq_lens contract as the other runs.
+ *
+ * Shape bounds (host only):
+ *   num_seqs, num_q_heads (1..128), page_size (16/32/64/128), num_pages,
+ *   page_table_cols, page_table_row_stride (>= cols), kv_page_stride
+ *   (elements between pages; 0 = page_size * 576), max_seq_len (0 = cols *
+ *   page_size), num_splits (0 = heuristic, >= 1 forced), num_cus (0 = query
+ *   the device)
+ */
+typedef struct {
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t page_size;
+  int32_t num_pages;
+  int32_t page_table_cols;
+  int32_t page_table_row_stride;
+  int64_t kv_page_stride;
+  int32_t max_seq_len;
+  int32_t num_splits;
+  int32_t num_cus;
+} pa_mla_desc;
+
+typedef struct pa_mla_plan_s* pa_mla_plan_t;
+
+/*
+ * Per-run arguments (device pointers unless stated):
+ *   q           bf16 [B, Hq, 576] (absorbed latent query, then RoPE query),
+ *               16-byte aligned; q_stride_t elements between sequences
+ *               (0 = Hq * 576), multiple of 8
+ *   kv_cache    bf16 [P, page_size, 576], 16-byte aligned
+ *   page_table  int32 [B, row_stride];  seq_lens int32 [B]
+ *   softmax_scale  host float > 0;  softcap host float >= 0 (0 = off)
+ *   out         bf16 [B, Hq, 512], 16-byte aligned; o_stride_t elements between
+ *               sequences (0 = Hq * 512), multiple of 8
+ *   lse         fp32 [B, Hq] natural log, or NULL
+ *   workspace   at least pa_mla_workspace_bytes(plan) bytes, 256-byte aligned
+ * Errors: PA_ERR_INVALID for NULL/misaligned pointers, bad strides or scales;
+ * PA_ERR_WORKSPACE for a missing or short workspace; PA_ERR_HIP for a failed
+ * launch.  Asynchronous on `stream`; no allocation, no host synchronisation.
+ */
+typedef struct {
+  const void* q;
+  int64_t q_stride_t;
+  const void* kv_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  float softmax_scale;
+  float softcap;
+  void* out;
+  int64_t o_stride_t;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+} pa_mla_args;
+
+/* Validate an MLA shape description and build its plan (PA_ERR_INVALID,
+ * PA_ERR_UNSUPPORTED as for pa_plan). */
+pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out);
+/* Workspace bytes a run of this plan needs (0 when it does not split). */
+size_t pa_mla_workspace_bytes(pa_mla_plan_t plan);
+/* Split-KV factor the plan chose. */
+int32_t pa_mla_num_splits(pa_mla_plan_t plan);
+/* Run MLA decode: one main launch, plus the log-sum-exp merge when split. */
+pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* args, hipStream_t stream);
+/* Release an MLA plan (NULL is ignored). */
+void pa_mla_plan_destroy(pa_mla_plan_t plan);
+
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status status);
 

@@ -92,3 +92,54 @@ class PagedAttention:
               "mixed": B.pa_run_mixed}[mode]
         fn(self.plan, a, s)
         return out, lse
+
+
+class MlaDecode:
+    """An MLA decode plan for one latent-cache workload shape plus its workspace."""
+
+    def __init__(self, w, *, num_splits: int = 0, num_cus: int = 0, device="cuda"):
+        self.w = w
+        self.device = torch.device(device)
+        self.desc = B.pa_mla_desc(num_seqs=w.num_seqs, num_q_heads=w.num_q_heads,
+                                  page_size=w.page_size, num_pages=w.num_pages,
+                                  page_table_cols=w.pt_cols,
+                                  page_table_row_stride=int(w.page_table.shape[1]),
+                                  kv_page_stride=0, max_seq_len=w.max_seq_len,
+                                  num_splits=num_splits, num_cus=num_cus)
+        self.plan = B.pa_mla_plan(self.desc)
+        self.num_splits = B.pa_mla_num_splits(self.plan)
+        nbytes = B.pa_mla_workspace_bytes(self.plan)
+        self.workspace = (torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                          if nbytes else None)
+        self.q = w.q.to(self.device)
+        self.kv = w.kv.to(self.device)
+        self.page_table = w.page_table.to(self.device)
+        self.seq_lens = w.seq_lens.to(self.device)
+
+    def __del__(self):
+        plan = getattr(self, "plan", None)
+        if plan is not None:
+            try:
+                B.pa_mla_plan_destroy(plan)
+            except Exception:
+                pass
+            self.plan = None
+
+    def new_outputs(self):
+        out = torch.empty((self.w.num_seqs, self.w.num_q_heads, 512), dtype=torch.bfloat16,
+                          device=self.device)
+        lse = torch.empty((self.w.num_seqs, self.w.num_q_heads), dtype=torch.float32,
+                          device=self.device)
+        return out, lse
+
+    def args(self, out, lse):
+        return B.make_mla_args(q=self.q, kv_cache=self.kv, page_table=self.page_table,
+                               seq_lens=self.seq_lens, softmax_scale=self.w.scale, out=out,
+                               lse=lse, workspace=self.workspace, softcap=self.w.softcap)
+
+    def run(self, out=None, lse=None, stream=None):
+        if out is None:
+            out, lse = self.new_outputs()
+        B.pa_run_mla_decode(self.plan, self.args(out, lse),
+                            B.current_stream() if stream is None else stream)
+        return out, lse

@@ -8,6 +8,9 @@ stream.  The functions keep the C names:
     pa_plan_get_info(plan) -> info   pa_plan_destroy(plan)
     pa_run_prefill / pa_run_decode / pa_run_mixed(plan, args, stream) -> None
     pa_run_append(plan, append_args, stream) -> None
+    pa_mla_plan(mla_desc) -> plan    pa_mla_workspace_bytes(plan) -> int
+    pa_mla_num_splits(plan) -> int   pa_mla_plan_destroy(plan)
+    pa_run_mla_decode(plan, mla_args, stream) -> None
     pa_status_str(code) -> str
 
 Errors are raised as ``PaError`` carrying the status code.  If libpa.so has not
@@ -32,7 +35,9 @@ PA_KV_BF16 = 0
 PA_KV_FP8_E4M3 = 1
 
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
-           "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str")
+           "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str",
+           "pa_mla_plan", "pa_mla_workspace_bytes", "pa_mla_num_splits", "pa_run_mla_decode",
+           "pa_mla_plan_destroy")
 
 
 class PaLibraryMissing(RuntimeError):
@@ -115,6 +120,38 @@ class pa_append_args(ctypes.Structure):
     ]
 
 
+class pa_mla_desc(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_table_cols", ctypes.c_int32),
+        ("page_table_row_stride", ctypes.c_int32),
+        ("kv_page_stride", ctypes.c_int64),
+        ("max_seq_len", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+    ]
+
+
+class pa_mla_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("q_stride_t", ctypes.c_int64),
+        ("kv_cache", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("o_stride_t", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -144,6 +181,16 @@ def lib():
         L.pa_plan_destroy.restype = None
         L.pa_status_str.argtypes = [ctypes.c_int]
         L.pa_status_str.restype = ctypes.c_char_p
+        L.pa_mla_plan.argtypes = [ctypes.POINTER(pa_mla_desc), ctypes.POINTER(vp)]
+        L.pa_mla_plan.restype = ctypes.c_int
+        L.pa_mla_workspace_bytes.argtypes = [vp]
+        L.pa_mla_workspace_bytes.restype = ctypes.c_size_t
+        L.pa_mla_num_splits.argtypes = [vp]
+        L.pa_mla_num_splits.restype = ctypes.c_int32
+        L.pa_run_mla_decode.argtypes = [vp, ctypes.POINTER(pa_mla_args), vp]
+        L.pa_run_mla_decode.restype = ctypes.c_int
+        L.pa_mla_plan_destroy.argtypes = [vp]
+        L.pa_mla_plan_destroy.restype = None
         _lib = L
     return _lib
 
@@ -249,3 +296,41 @@ def make_append_args(*, k_new, v_new, cu_new, seq_lens, page_table, k_pool, v_po
 def current_stream() -> int:
     import torch
     return int(torch.cuda.current_stream().cuda_stream)
+
+
+def pa_mla_plan(desc: pa_mla_desc) -> ctypes.c_void_p:
+    plan = ctypes.c_void_p()
+    rc = lib().pa_mla_plan(ctypes.byref(desc), ctypes.byref(plan))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_mla_plan")
+    return plan
+
+
+def pa_mla_workspace_bytes(plan) -> int:
+    return int(lib().pa_mla_workspace_bytes(plan))
+
+
+def pa_mla_num_splits(plan) -> int:
+    return int(lib().pa_mla_num_splits(plan))
+
+
+def pa_run_mla_decode(plan, args: pa_mla_args, stream) -> None:
+    rc = lib().pa_run_mla_decode(plan, ctypes.byref(args), ctypes.c_void_p(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_run_mla_decode")
+
+
+def pa_mla_plan_destroy(plan) -> None:
+    lib().pa_mla_plan_destroy(plan)
+
+
+def make_mla_args(*, q, kv_cache, page_table, seq_lens, softmax_scale: float, out, lse=None,
+                  workspace=None, softcap: float = 0.0, q_stride_t: int = 0,
+                  o_stride_t: int = 0) -> pa_mla_args:
+    """Build pa_mla_args from device tensors."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return pa_mla_args(q=_ptr(q), q_stride_t=q_stride_t, kv_cache=_ptr(kv_cache),
+                       page_table=_ptr(page_table), seq_lens=_ptr(seq_lens),
+                       softmax_scale=float(softmax_scale), softcap=float(softcap), out=_ptr(out),
+                       o_stride_t=o_stride_t, lse=_ptr(lse), workspace=_ptr(workspace),
+                       workspace_bytes=ws_bytes)

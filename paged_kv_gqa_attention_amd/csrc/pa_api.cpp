@@ -364,3 +364,162 @@ pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream) 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// MLA decode
+// ---------------------------------------------------------------------------
+
+namespace {
+constexpr int kMlaDk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kMlaMinSplitKeys = 256;     // a window of at least 8 key tiles
+}  // namespace
+
+struct pa_mla_plan_s {
+  pa_mla_desc d;
+  int32_t page_shift;
+  int32_t num_splits;
+  int32_t split_keys;
+  int32_t head_groups;
+  int64_t kv_page_bytes;
+  size_t part_o_bytes;
+  size_t ws_bytes;
+};
+
+extern "C" {
+
+pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out) {
+  if (!desc || !out) return PA_ERR_INVALID;
+  const pa_mla_desc& d = *desc;
+  if (d.num_seqs < 0 || d.num_q_heads <= 0 || d.page_size <= 0 || d.num_pages < 0 ||
+      d.page_table_cols < 0 || d.page_table_row_stride < d.page_table_cols || d.kv_page_stride < 0 ||
+      d.max_seq_len < 0 || d.num_splits < 0 || d.num_cus < 0)
+    return PA_ERR_INVALID;
+  if (d.num_q_heads > 128) return PA_ERR_UNSUPPORTED;
+  if (d.page_size != 16 && d.page_size != 32 && d.page_size != 64 && d.page_size != 128)
+    return PA_ERR_UNSUPPORTED;
+  const int64_t dense_page = (int64_t)d.page_size * kMlaDk;
+  const int64_t page_elems = d.kv_page_stride ? d.kv_page_stride : dense_page;
+  if (page_elems < dense_page || (page_elems * 2) % 16 != 0) return PA_ERR_INVALID;
+  const int64_t capacity = (int64_t)d.page_table_cols * d.page_size;
+  if (capacity > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
+  if (d.max_seq_len > capacity) return PA_ERR_INVALID;
+  int cus = d.num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return PA_ERR_HIP;
+    if (cus <= 0) return PA_ERR_HIP;
+  }
+  pa_mla_plan_s* p = new (std::nothrow) pa_mla_plan_s;
+  if (!p) return PA_ERR_INVALID;
+  p->d = d;
+  p->page_shift = ilog2(d.page_size);
+  p->kv_page_bytes = page_elems * 2;
+  p->head_groups = d.num_q_heads <= 64 ? 1 : (int32_t)ceil_div(d.num_q_heads, 64);
+  // Split so that the items (sequence, window, head group) fill the device in
+  // one round (one workgroup fits on a compute unit; a partial second round
+  // measured slower than fewer, longer windows), in windows of at least
+  // kMlaMinSplitKeys keys.
+  const int64_t max_len = d.max_seq_len ? d.max_seq_len : capacity;
+  int splits = d.num_splits;
+  if (splits == 0) {
+    const int64_t items = std::max<int64_t>(1, (int64_t)d.num_seqs * p->head_groups);
+    const int64_t want = std::max<int64_t>(1, (int64_t)cus / items);
+    const int64_t by_len = std::max<int64_t>(1, max_len / kMlaMinSplitKeys);
+    splits = (int)std::max<int64_t>(1, std::min(want, by_len));
+  }
+  const int64_t span = std::max<int64_t>(max_len, 1);
+  int64_t split_keys = ceil_div(span, splits);
+  split_keys = std::max<int64_t>(kSplitAlign, ceil_div(split_keys, kSplitAlign) * kSplitAlign);
+  splits = (int)std::max<int64_t>(1, ceil_div(span, split_keys));
+  p->num_splits = splits;
+  p->split_keys = (int32_t)(splits > 1 ? split_keys : std::max<int64_t>(capacity, kSplitAlign));
+  if (splits > 1) {
+    const size_t rows = (size_t)splits * (size_t)d.num_seqs * (size_t)d.num_q_heads;
+    p->part_o_bytes = align_up(rows * kMlaDv * sizeof(float), kWsAlign);
+    p->ws_bytes = p->part_o_bytes + align_up(rows * sizeof(float), kWsAlign);
+  } else {
+    p->part_o_bytes = 0;
+    p->ws_bytes = 0;
+  }
+  *out = p;
+  return PA_OK;
+}
+
+size_t pa_mla_workspace_bytes(pa_mla_plan_t plan) { return plan ? plan->ws_bytes : 0; }
+
+int32_t pa_mla_num_splits(pa_mla_plan_t plan) { return plan ? plan->num_splits : 0; }
+
+pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* a, hipStream_t stream) {
+  if (!plan || !a) return PA_ERR_INVALID;
+  const pa_mla_desc& d = plan->d;
+  const int64_t qrow = (int64_t)d.num_q_heads * kMlaDk;
+  const int64_t orow = (int64_t)d.num_q_heads * kMlaDv;
+  const int64_t q_stride = a->q_stride_t ? a->q_stride_t : qrow;
+  const int64_t o_stride = a->o_stride_t ? a->o_stride_t : orow;
+  if (q_stride < qrow || o_stride < orow || q_stride % 8 || o_stride % 8) return PA_ERR_INVALID;
+  if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 3.0e38f)) return PA_ERR_INVALID;
+  if (!(a->softcap >= 0.f) || !(a->softcap < 3.0e38f)) return PA_ERR_INVALID;
+  if (d.num_seqs == 0) return PA_OK;
+  if (!a->q || !a->kv_cache || !a->page_table || !a->seq_lens || !a->out) return PA_ERR_INVALID;
+  if (!aligned16(a->q) || !aligned16(a->kv_cache) || !aligned16(a->out)) return PA_ERR_INVALID;
+  const bool split = plan->num_splits > 1;
+  if (split) {
+    if (!a->workspace || a->workspace_bytes < plan->ws_bytes) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(a->workspace) & (kWsAlign - 1)) != 0) return PA_ERR_INVALID;
+  }
+  pa::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_stride_t = q_stride;
+  p.k_pool = static_cast<const uint8_t*>(a->kv_cache);
+  p.v_pool = p.k_pool;
+  p.kv_page_bytes = plan->kv_page_bytes;
+  p.page_table = a->page_table;
+  p.pt_row_stride = d.page_table_row_stride;
+  p.pt_cols = d.page_table_cols;
+  p.seq_lens = a->seq_lens;
+  p.num_seqs = d.num_seqs;
+  p.num_q_heads = d.num_q_heads;
+  p.num_kv_heads = 1;
+  p.group = d.num_q_heads;
+  p.page_shift = plan->page_shift;
+  p.causal = 1;
+  p.scale_log2 = a->softmax_scale * 1.4426950408889634f;
+  p.softcap = a->softcap;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.o_stride_t = o_stride;
+  p.lse = a->lse;
+  p.num_splits = plan->num_splits;
+  p.split_keys = plan->split_keys;
+  p.max_total_q = d.num_seqs;
+  p.head_groups = plan->head_groups;
+  if (split) {
+    p.part_o = static_cast<float*>(a->workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan->part_o_bytes);
+  }
+  const int64_t blocks = (int64_t)d.num_seqs * plan->num_splits * plan->head_groups;
+  if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (pa::launch_mla(p, dim3((unsigned)blocks, 1, 1), stream) != hipSuccess) return PA_ERR_HIP;
+  if (split) {
+    pa::MergeParams m;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.num_splits = p.num_splits;
+    m.max_total_q = p.max_total_q;
+    m.num_q_heads = d.num_q_heads;
+    m.cu_q_lens = nullptr;
+    m.num_seqs = d.num_seqs;
+    m.out = p.out;
+    m.o_stride_t = p.o_stride_t;
+    m.lse = p.lse;
+    if (pa::launch_merge(kMlaDv, m, stream) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+void pa_mla_plan_destroy(pa_mla_plan_t plan) { delete plan; }
+
+}  // extern "C"

@@ -50,6 +50,7 @@ struct AttnParams {
   int32_t q_block_tokens;       // tokens per q-block (prefill / mixed)
   int32_t balanced;             // decode only: persistent balanced schedule (see launch)
   int32_t* sched;               // balanced: [4 + B + 1] ints of workspace (unit offsets)
+  int32_t head_groups;          // MLA: groups of up to 64 query heads per item
 };
 
 struct MergeParams {
@@ -101,6 +102,11 @@ struct BalancedMergeParams {
   float* lse;
 };
 
+// Launch the MLA decode kernel (head dim 576 / value dim 512, one KV head) on a
+// one-dimensional grid of B * num_splits * head_groups workgroups; partials
+// (splits > 1) use the split-KV layout with head dim 512 and are merged by
+// launch_merge(512, ...).
+hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream);
 // Launch the merge of balanced decode pieces.
 hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream);
 

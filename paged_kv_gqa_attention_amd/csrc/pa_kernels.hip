@@ -1389,6 +1389,356 @@ void attn_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// MLA decode: one logical KV head whose 576-wide cached row (512 latent
+// values, then the 64-wide RoPE key) is the key, and whose latent part is the
+// value; up to 128 query heads share it
+// ---------------------------------------------------------------------------
+
+constexpr int kMlaLatent = 512;
+constexpr int kMlaDk = 576;
+
+// One 32-key tile of latent rows at a 1168-byte pitch (72 data slots of 16
+// bytes and a pad slot per row), rounded up to whole 1 KB direct loads.
+struct MlaGeo {
+  static constexpr int row_bytes = kMlaDk * 2;
+  static constexpr int chunks = row_bytes / 16;
+  static constexpr int pitch = row_bytes + 16;
+  static constexpr int slots = pitch / 16;
+  static constexpr int loads = (kSub * slots + 63) / 64;
+  static constexpr int tile_bytes = loads * 1024;
+  static constexpr int per_wave = (loads + kDecWaves - 1) / kDecWaves;
+  static constexpr int min_per_wave = loads / kDecWaves;
+};
+
+// Direct global->LDS loads of one 32-key tile: load i writes slots
+// [64 i, 64 i + 64) of the tile; lane l fetches the 16 bytes that belong at
+// slot 64 i + l (a pad slot, or a slot past the 32 rows, re-fetches chunk 0 of
+// row 31: in bounds, never read).  Wave w issues loads w, w + 4, ...
+struct MlaLoads {
+  uint32_t slot_rc[MlaGeo::per_wave];   // row in the tile (high half), byte offset in the row
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < MlaGeo::per_wave; ++j) {
+      const int slot = 64 * (wave + j * kDecWaves) + lane;
+      int row = slot / MlaGeo::slots;
+      int ch = slot - row * MlaGeo::slots;
+      if (row >= kSub) {
+        row = kSub - 1;
+        ch = 0;
+      }
+      slot_rc[j] = ((uint32_t)row << 16) | (ch < MlaGeo::chunks ? (uint32_t)ch * 16u : 0u);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ pool, const PageWalk& w, int key0,
+                                        uint8_t* buf, int wave) const {
+    const int slot_mask = (1 << w.shift) - 1;
+    if (w.shift >= 5 && key0 + kSub <= w.kend) {
+      // the tile's 32 keys are whole and share one page (key0 is a multiple
+      // of 32): one page id, then each load is that row's base plus the
+      // lane's offset
+      const uint8_t* base = pool + (int64_t)w.pcache[(key0 >> w.shift) - w.first_page] * w.page_bytes +
+                            (uint32_t)(key0 & slot_mask) * (uint32_t)MlaGeo::row_bytes;
+#pragma unroll
+      for (int j = 0; j < MlaGeo::per_wave; ++j) {
+        const int i = wave + j * kDecWaves;
+        if (i < MlaGeo::loads)
+          dma_load_16(base + ((slot_rc[j] >> 16) * (uint32_t)MlaGeo::row_bytes + (slot_rc[j] & 0xFFFFu)),
+                      buf + 1024 * i);
+      }
+      return;
+    }
+    int key[MlaGeo::per_wave], page[MlaGeo::per_wave];
+#pragma unroll
+    for (int j = 0; j < MlaGeo::per_wave; ++j) {
+      key[j] = min(key0 + (int)(slot_rc[j] >> 16), w.kend - 1);
+      page[j] = w.pcache[(key[j] >> w.shift) - w.first_page];
+    }
+#pragma unroll
+    for (int j = 0; j < MlaGeo::per_wave; ++j) {
+      const int i = wave + j * kDecWaves;
+      if (i < MlaGeo::loads) {
+        const uint8_t* src = pool + (int64_t)page[j] * w.page_bytes +
+                             ((uint32_t)(key[j] & slot_mask) * (uint32_t)MlaGeo::row_bytes + (slot_rc[j] & 0xFFFFu));
+        dma_load_16(src, buf + 1024 * i);
+      }
+    }
+  }
+};
+
+// LDS of an MLA workgroup with NCT row tiles: the exchange buffer for the
+// waves' partial scores, then as many tile buffers as fit.
+template <int NCT>
+struct MlaLds {
+  static constexpr int xbuf_bytes = kDecWaves * NCT * 4 * kWave * 16;   // partial scores
+  static constexpr int pbuf_bytes = NCT * 2 * kWave * 16;               // bf16 probabilities
+  static constexpr int ring = (kLdsMax - 64 - kPcacheEntries * 4 - xbuf_bytes - pbuf_bytes) / MlaGeo::tile_bytes;
+  static constexpr int xbuf_off = ring * MlaGeo::tile_bytes;
+  static constexpr int pbuf_off = xbuf_off + xbuf_bytes;
+  static constexpr int pcache_off = pbuf_off + pbuf_bytes + 64;
+  static constexpr int bytes = pcache_off + kPcacheEntries * 4;
+  static_assert(ring >= 2 && bytes <= kLdsMax, "MLA LDS budget exceeded");
+};
+
+// One soft-capped value (same formula as cap_tile).
+__device__ __forceinline__ float cap1(float x, const SoftCap& sc) {
+  const float e = __builtin_amdgcn_exp2f(x * sc.k2);
+  return __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f) * sc.inv_b;
+}
+
+// The key loop of an MLA item (see mla_kernel).  CAP selects soft-capping at
+// compile time so that uncapped runs carry none of its work.
+template <int NCT, bool CAP>
+__device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
+                                         int klo, int khi, const bf16x8 (&qreg)[NCT][kMlaDk / 16 / kDecWaves],
+                                         float c, const SoftCap& sc,
+                                         SoftmaxState<kMlaLatent / kDecWaves> (&st)[NCT], int wave, int lane) {
+  using LD = MlaLds<NCT>;
+  constexpr int R = LD::ring;
+  constexpr int QJ = kMlaDk / 16 / kDecWaves;       // score k-steps per wave
+  constexpr int VT = kMlaLatent / 32 / kDecWaves;   // value tiles per wave
+  uint8_t* xbuf = smem + LD::xbuf_off;
+  uint8_t* pbuf = smem + LD::pbuf_off;
+  PageWalk w;
+  w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
+  w.page_bytes = p.kv_page_bytes;
+  w.head_off = 0;
+  w.row_stride_b = MlaGeo::row_bytes;
+  w.shift = p.page_shift;
+  w.klimit = L;
+  MlaLoads ml;
+  ml.init(wave, lane);
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    wait_vmem_all();                            // Q loads and page-table reads
+    __syncthreads();
+    const int ntiles = (ce - cb + kSub - 1) / kSub;
+#pragma unroll
+    for (int t = 0; t < R - 1; ++t)
+      if (t < ntiles) ml.issue(p.k_pool, w, cb + t * kSub, smem + t * MlaGeo::tile_bytes, wave);
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t must have landed; up to R-2 later tiles may stay in flight
+      if (R >= 3 && t + 1 < ntiles)
+        wait_vmem<(R >= 3 ? MlaGeo::min_per_wave : 0)>();
+      else
+        wait_vmem<0>();
+      ring_barrier();
+      if (t + R - 1 < ntiles)
+        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
+      const uint8_t* kl = smem + (t % R) * MlaGeo::tile_bytes;
+      // partial scores over this wave's columns
+      f32x16 s[NCT];
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[rt][i] = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < QJ; ++jj) {
+        const bf16x8 a = k_operand<kMlaDk, false, MlaGeo::pitch>(kl, 0, QJ * wave + jj, lane);
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt) s[rt] = mfma32(a, qreg[rt][jj], s[rt]);
+      }
+      // exchange: 16-byte records [wave][row tile][quarter][lane]; every wave
+      // sums the four partials in the same order, so all hold identical scores
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(xbuf + (((wave * NCT + rt) * 4 + q4) * kWave + lane) * 16) =
+              f32x4{s[rt][4 * q4], s[rt][4 * q4 + 1], s[rt][4 * q4 + 2], s[rt][4 * q4 + 3]};
+      ring_barrier();
+      f32x16 sf[NCT];
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sf[rt][i] = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) {
+#pragma unroll
+        for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(xbuf + (((w2 * NCT + rt) * 4 + q4) * kWave + lane) * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sf[rt][4 * q4 + e] += v[e];
+          }
+        if (NCT > 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      const int k0 = cb + t * kSub;
+      // Softmax split over the waves: all of them form the row max (identical
+      // scores give identical running state), each forms the probabilities of
+      // its quarter of the tile (accumulator elements 4 wave .. 4 wave + 3 of
+      // every lane) and keeps its own partial row sum; the bf16 probabilities
+      // meet in LDS as the PV operand.
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt) {
+        if (k0 + kSub > khi) mask_tile(sf[rt], k0, khi, lane);
+        float mx = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sf[rt][i], sf[rt][i + 1]));
+        mx = fmaxf(mx, xor32(mx));
+        float mxs = mx * c;
+        if constexpr (CAP) mxs = mx == neg_inf() ? neg_inf() : cap1(mx, sc) * c;   // tanh is monotonic
+        if (__builtin_amdgcn_ballot_w64(mxs > st[rt].m + kRescaleSlack)) {
+          const float m_new = fmaxf(st[rt].m, mxs);
+          const float alpha = __builtin_amdgcn_exp2f(st[rt].m - (m_new == neg_inf() ? 0.f : m_new));
+          st[rt].l *= alpha;
+#pragma unroll
+          for (int tt = 0; tt < VT; ++tt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) st[rt].o[tt][i] *= alpha;
+          st[rt].m = m_new;
+        }
+        const float nref = st[rt].m == neg_inf() ? 0.f : -st[rt].m;
+        float pq[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // element 4 wave + e, picked with wave-uniform selects
+          float v = wave == 0 ? sf[rt][e] : wave == 1 ? sf[rt][4 + e] : wave == 2 ? sf[rt][8 + e] : sf[rt][12 + e];
+          if constexpr (CAP) v = v == neg_inf() ? neg_inf() : cap1(v, sc);
+          pq[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v, c, nref));
+        }
+        st[rt].l += (pq[0] + pq[1]) + (pq[2] + pq[3]);
+        *reinterpret_cast<u32x2*>(pbuf + ((rt * 2 + (wave >> 1)) * kWave + lane) * 16 + (wave & 1) * 8) =
+            u32x2{pack_bf16x2(pq[0], pq[1]), pack_bf16x2(pq[2], pq[3])};
+      }
+      ring_barrier();
+      bf16x8 pb[NCT][2];
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          pb[rt][hh] = as_bf16x8(*reinterpret_cast<const u32x4*>(pbuf + ((rt * 2 + hh) * kWave + lane) * 16));
+      // O^T += V^T P^T over this wave's value columns of the same tile
+#pragma unroll
+      for (int tt = 0; tt < VT; ++tt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 a = v_operand<false, MlaGeo::pitch>(kl, 0, VT * wave + tt, hh, lane);
+#pragma unroll
+          for (int rt = 0; rt < NCT; ++rt) st[rt].o[tt] = mfma32(a, pb[rt][hh], st[rt].o[tt]);
+        }
+    }
+  }
+}
+
+// Item = (sequence b, split window, head group of up to 64 query heads), NCT
+// 32-row tiles of query heads.  The four waves split the work by columns:
+// wave w contracts columns [144 w, 144 w + 144) of q.C for every row tile
+// (its 36 query values per row in registers), the partial scores are summed
+// through LDS so that every wave holds the same full scores, the softmax is
+// split four ways (mla_keys), and wave w accumulates the value columns
+// [128 w, 128 w + 128).  No product is computed twice.  More than 64 heads
+// take several head groups (their score and accumulator registers would not
+// fit one wave).  The grid is one-dimensional; items are ordered (b, split,
+// group) and dealt so that each XCD takes a contiguous run of them, which puts
+// the head groups of one window on one L2.
+template <int NCT>
+__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_kernel(AttnParams p) {
+  using LD = MlaLds<NCT>;
+  constexpr int QJ = kMlaDk / 16 / kDecWaves;
+  constexpr int VT = kMlaLatent / 32 / kDecWaves;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
+  int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int hg, b, split;
+  {
+    const int n = gridDim.x;
+    const int lin = blockIdx.x;
+    const int full = n - n % kXcds;
+    const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
+    hg = logical % p.head_groups;
+    const int rest = logical / p.head_groups;
+    split = rest % p.num_splits;
+    b = rest / p.num_splits;
+  }
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  const int klo = split * p.split_keys;
+  // the last window takes every remaining key
+  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
+
+  // this wave's query columns of every row tile
+  bf16x8 qreg[NCT][QJ];
+#pragma unroll
+  for (int rt = 0; rt < NCT; ++rt) {
+    const int h = (hg * NCT + rt) * kCols + (lane & 31);
+    const bool ok = h < p.num_q_heads;
+    const uint16_t* src = p.q + (int64_t)b * p.q_stride_t + (int64_t)(ok ? h : 0) * kMlaDk +
+                          16 * QJ * wave + (lane >> 5) * 8;
+#pragma unroll
+    for (int jj = 0; jj < QJ; ++jj) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * jj);
+      qreg[rt][jj] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  float c, vdesc;
+  score_scales<false>(p, c, vdesc);
+  const SoftCap sc(p.softcap, c);
+  SoftmaxState<VT * 32> st[NCT];
+#pragma unroll
+  for (int rt = 0; rt < NCT; ++rt) state_init(st[rt]);
+  if (khi > klo) {
+    if (sc.on())
+      mla_keys<NCT, true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
+    else
+      mla_keys<NCT, false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
+  }
+  // full row sums: each wave holds the sum over its quarter of the keys
+  float* lsum = reinterpret_cast<float*>(smem + LD::xbuf_off);
+  __syncthreads();
+#pragma unroll
+  for (int rt = 0; rt < NCT; ++rt) lsum[(wave * NCT + rt) * kWave + lane] = st[rt].l + xor32(st[rt].l);
+  __syncthreads();
+  const int d_base = VT * 32 * wave;
+#pragma unroll
+  for (int rt = 0; rt < NCT; ++rt) {
+    const int h = (hg * NCT + rt) * kCols + (lane & 31);
+    float l_tot = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kDecWaves; ++w2) l_tot += lsum[(w2 * NCT + rt) * kWave + lane];
+    if (h >= p.num_q_heads) continue;
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : vdesc / l_tot;
+    const float lse2 = empty ? neg_inf() : st[rt].m + __builtin_amdgcn_logf(l_tot);
+    if (p.num_splits > 1) {
+      const int64_t row = ((int64_t)split * p.max_total_q + b) * p.num_q_heads + h;
+      if (wave == 0 && (lane >> 5) == 0) p.part_lse[row] = lse2;
+      if (empty) continue;
+      float* dst = p.part_o + row * kMlaLatent + d_base;
+#pragma unroll
+      for (int tt = 0; tt < VT; ++tt)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
+          f32x4 v;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = st[rt].o[tt][4 * ig + k] * inv;
+          *reinterpret_cast<f32x4*>(dst + d0) = v;
+        }
+    } else {
+      uint16_t* dst = p.out + (int64_t)b * p.o_stride_t + (int64_t)h * kMlaLatent + d_base;
+#pragma unroll
+      for (int tt = 0; tt < VT; ++tt)
+#pragma unroll
+        for (int ig = 0; ig < 4; ++ig) {
+          const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
+          const u32x2 v{pack_bf16x2(st[rt].o[tt][4 * ig] * inv, st[rt].o[tt][4 * ig + 1] * inv),
+                        pack_bf16x2(st[rt].o[tt][4 * ig + 2] * inv, st[rt].o[tt][4 * ig + 3] * inv)};
+          *reinterpret_cast<u32x2*>(dst + d0) = v;
+        }
+      if (p.lse && wave == 0 && (lane >> 5) == 0) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // split-KV merge: LSE = log sum exp(LSE_s), O = sum exp(LSE_s - LSE) O_s
 // ---------------------------------------------------------------------------
 
@@ -1708,6 +2058,15 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  const dim3 block(kDecWaves * kWave);
+  if (p.num_q_heads <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, block, 0, stream, p);
+  else if (p.num_q_heads <= 128) hipLaunchKernelGGL(mla_kernel<2>, grid, block, 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.num_seqs * p.num_q_heads;
   const dim3 grid((unsigned)((rows + 3) / 4));
@@ -1729,6 +2088,7 @@ hipError_t launch_merge(int head_dim, const MergeParams& p, hipStream_t stream) 
     case 64: hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, p); break;
     case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, stream, p); break;
     case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, p); break;
+    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

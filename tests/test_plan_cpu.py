@@ -196,3 +196,44 @@ def test_append_rejects_bad_arguments_without_touching_the_device():
     p = B.pa_plan(desc(num_seqs=0))                      # nothing to append: no launch
     assert B.lib().pa_run_append(p, ctypes.byref(B.pa_append_args()), None) == B.PA_OK
     B.pa_plan_destroy(p)
+
+
+def test_mla_plan():
+    def mdesc(**kw):
+        d = dict(num_seqs=64, num_q_heads=16, page_size=32, num_pages=4000, page_table_cols=64,
+                 page_table_row_stride=64, kv_page_stride=0, max_seq_len=2048, num_splits=0,
+                 num_cus=256)
+        d.update(kw)
+        return B.pa_mla_desc(**d)
+    # one round of workgroups: 64 sequences x 4 windows on 256 CUs
+    p = B.pa_mla_plan(mdesc())
+    assert B.pa_mla_num_splits(p) == 4
+    assert B.pa_mla_workspace_bytes(p) >= 4 * 64 * 16 * (512 + 1) * 4
+    B.pa_mla_plan_destroy(p)
+    # 128 heads take two head groups: two windows fill the round
+    p = B.pa_mla_plan(mdesc(num_q_heads=128))
+    assert B.pa_mla_num_splits(p) == 2
+    B.pa_mla_plan_destroy(p)
+    # many sequences: no split, no workspace
+    p = B.pa_mla_plan(mdesc(num_seqs=512))
+    assert B.pa_mla_num_splits(p) == 1 and B.pa_mla_workspace_bytes(p) == 0
+    B.pa_mla_plan_destroy(p)
+    for bad, code in ((dict(num_q_heads=129), B.PA_ERR_UNSUPPORTED), (dict(page_size=8), B.PA_ERR_UNSUPPORTED),
+                      (dict(num_q_heads=0), B.PA_ERR_INVALID), (dict(max_seq_len=5000), B.PA_ERR_INVALID),
+                      (dict(kv_page_stride=100), B.PA_ERR_INVALID)):
+        with pytest.raises(B.PaError) as e:
+            B.pa_mla_plan(mdesc(**bad))
+        assert e.value.code == code
+    # runs reject bad arguments before touching the device
+    p = B.pa_mla_plan(mdesc())
+    assert B.lib().pa_run_mla_decode(p, None, None) == B.PA_ERR_INVALID
+    a = B.pa_mla_args(q=4096, kv_cache=8192, page_table=12288, seq_lens=16384, out=20480,
+                      softmax_scale=0.1)
+    assert B.lib().pa_run_mla_decode(p, ctypes.byref(a), None) == B.PA_ERR_WORKSPACE
+    for field, val in (("q", 4100), ("softmax_scale", -1.0), ("softcap", float("nan")),
+                       ("q_stride_t", 12)):
+        x = B.pa_mla_args(q=4096, kv_cache=8192, page_table=12288, seq_lens=16384, out=20480,
+                          softmax_scale=0.1, workspace=1 << 20, workspace_bytes=1 << 30)
+        setattr(x, field, val)
+        assert B.lib().pa_run_mla_decode(p, ctypes.byref(x), None) == B.PA_ERR_INVALID
+    B.pa_mla_plan_destroy(p)
