@@ -287,8 +287,10 @@ void pa_plan_destroy(pa_plan_t plan);
  *   num_seqs, num_q_heads (1..128), page_size (16/32/64/128), num_pages,
  *   page_table_cols, page_table_row_stride (>= cols), kv_page_stride
  *   (elements between pages; 0 = page_size * 576), max_seq_len (0 = cols *
- *   page_size), num_splits (0 = heuristic, >= 1 forced), num_cus (0 = query
- *   the device)
+ *   page_size), num_splits (0 = heuristic, >= 1 forced, -1 = balanced: one
+ *   workgroup per compute unit, each streaming an equal share of all keys,
+ *   items cut between workgroups merged afterwards), num_cus (0 = query the
+ *   device)
  */
 typedef struct {
   int32_t num_seqs;
@@ -341,7 +343,7 @@ typedef struct {
 pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out);
 /* Workspace bytes a run of this plan needs (0 when it does not split). */
 size_t pa_mla_workspace_bytes(pa_mla_plan_t plan);
-/* Split-KV factor the plan chose. */
+/* Split-KV factor the plan chose (-1: the balanced schedule). */
 int32_t pa_mla_num_splits(pa_mla_plan_t plan);
 /* Run MLA decode: one main launch, plus the log-sum-exp merge when split. */
 pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* args, hipStream_t stream);

@@ -307,6 +307,7 @@ pa_status launch(pa_plan_t plan, const pa::AttnParams& p, pa::Mode mode, hipStre
     m.num_seqs = d.num_seqs;
     m.num_q_heads = d.num_q_heads;
     m.num_kv_heads = d.num_kv_heads;
+    m.rows_per_item = plan->group;
     m.max_total_q = p.max_total_q;
     m.cu_q_lens = p.cu_q_lens;
     m.out = p.out;
@@ -381,8 +382,11 @@ struct pa_mla_plan_s {
   int32_t num_splits;
   int32_t split_keys;
   int32_t head_groups;
+  int32_t group;              // query heads per head group
+  int32_t balanced_wgs;       // > 0: balanced schedule with this many workgroups
   int64_t kv_page_bytes;
   size_t part_o_bytes;
+  size_t part_lse_bytes;      // balanced layout only
   size_t ws_bytes;
 };
 
@@ -393,7 +397,7 @@ pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out) {
   const pa_mla_desc& d = *desc;
   if (d.num_seqs < 0 || d.num_q_heads <= 0 || d.page_size <= 0 || d.num_pages < 0 ||
       d.page_table_cols < 0 || d.page_table_row_stride < d.page_table_cols || d.kv_page_stride < 0 ||
-      d.max_seq_len < 0 || d.num_splits < 0 || d.num_cus < 0)
+      d.max_seq_len < 0 || d.num_splits < -1 || d.num_cus < 0)
     return PA_ERR_INVALID;
   if (d.num_q_heads > 128) return PA_ERR_UNSUPPORTED;
   if (d.page_size != 16 && d.page_size != 32 && d.page_size != 64 && d.page_size != 128)
@@ -418,6 +422,24 @@ pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out) {
   p->page_shift = ilog2(d.page_size);
   p->kv_page_bytes = page_elems * 2;
   p->head_groups = d.num_q_heads <= 64 ? 1 : (int32_t)ceil_div(d.num_q_heads, 64);
+  p->group = d.num_q_heads <= 64 ? d.num_q_heads : 64;
+  p->balanced_wgs = 0;
+  p->part_lse_bytes = 0;
+  if (d.num_splits == -1) {
+    // Balanced schedule: one workgroup per compute unit, equal key shares
+    // over all (sequence, head group) items; two partial records of `group`
+    // rows per workgroup, then the unit offsets.
+    p->balanced_wgs = cus;
+    p->num_splits = 1;
+    p->split_keys = (int32_t)std::max<int64_t>(capacity, kSplitAlign);
+    const size_t recs = (size_t)2 * cus * (size_t)p->group;
+    p->part_o_bytes = align_up(recs * kMlaDv * sizeof(float), kWsAlign);
+    p->part_lse_bytes = align_up(recs * sizeof(float), kWsAlign);
+    p->ws_bytes = p->part_o_bytes + p->part_lse_bytes +
+                  align_up((size_t)(4 + d.num_seqs + 1) * sizeof(int32_t), kWsAlign);
+    *out = p;
+    return PA_OK;
+  }
   // Split so that the items (sequence, window, head group) fill the device in
   // one round (one workgroup fits on a compute unit; a partial second round
   // measured slower than fewer, longer windows), in windows of at least
@@ -450,7 +472,10 @@ pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out) {
 
 size_t pa_mla_workspace_bytes(pa_mla_plan_t plan) { return plan ? plan->ws_bytes : 0; }
 
-int32_t pa_mla_num_splits(pa_mla_plan_t plan) { return plan ? plan->num_splits : 0; }
+int32_t pa_mla_num_splits(pa_mla_plan_t plan) {
+  if (!plan) return 0;
+  return plan->balanced_wgs > 0 ? -1 : plan->num_splits;
+}
 
 pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* a, hipStream_t stream) {
   if (!plan || !a) return PA_ERR_INVALID;
@@ -465,8 +490,9 @@ pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* a, hipStream_
   if (d.num_seqs == 0) return PA_OK;
   if (!a->q || !a->kv_cache || !a->page_table || !a->seq_lens || !a->out) return PA_ERR_INVALID;
   if (!aligned16(a->q) || !aligned16(a->kv_cache) || !aligned16(a->out)) return PA_ERR_INVALID;
+  const bool balanced = plan->balanced_wgs > 0;
   const bool split = plan->num_splits > 1;
-  if (split) {
+  if (split || balanced) {
     if (!a->workspace || a->workspace_bytes < plan->ws_bytes) return PA_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(a->workspace) & (kWsAlign - 1)) != 0) return PA_ERR_INVALID;
   }
@@ -496,9 +522,31 @@ pa_status pa_run_mla_decode(pa_mla_plan_t plan, const pa_mla_args* a, hipStream_
   p.split_keys = plan->split_keys;
   p.max_total_q = d.num_seqs;
   p.head_groups = plan->head_groups;
-  if (split) {
-    p.part_o = static_cast<float*>(a->workspace);
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + plan->part_o_bytes);
+  p.group = plan->group;
+  if (split || balanced) {
+    char* ws = static_cast<char*>(a->workspace);
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_lse = reinterpret_cast<float*>(ws + plan->part_o_bytes);
+  }
+  if (balanced) {
+    p.balanced = 1;
+    p.sched = reinterpret_cast<int32_t*>(static_cast<char*>(a->workspace) + plan->part_o_bytes +
+                                         plan->part_lse_bytes);
+    if (pa::launch_mla(p, dim3((unsigned)plan->balanced_wgs, 1, 1), stream) != hipSuccess) return PA_ERR_HIP;
+    pa::BalancedMergeParams m;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.sched = p.sched;
+    m.num_seqs = d.num_seqs;
+    m.num_q_heads = d.num_q_heads;
+    m.num_kv_heads = plan->head_groups;
+    m.rows_per_item = plan->group;
+    m.max_total_q = d.num_seqs;
+    m.cu_q_lens = nullptr;
+    m.out = p.out;
+    m.o_stride_t = p.o_stride_t;
+    m.lse = p.lse;
+    return pa::launch_merge_balanced(kMlaDv, m, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
   }
   const int64_t blocks = (int64_t)d.num_seqs * plan->num_splits * plan->head_groups;
   if (blocks > INT32_MAX) return PA_ERR_UNSUPPORTED;

@@ -50,7 +50,7 @@ struct AttnParams {
   int32_t q_block_tokens;       // tokens per q-block (prefill / mixed)
   int32_t balanced;             // decode only: persistent balanced schedule (see launch)
   int32_t* sched;               // balanced: [4 + B + 1] ints of workspace (unit offsets)
-  int32_t head_groups;          // MLA: groups of up to 64 query heads per item
+  int32_t head_groups;          // MLA: groups of up to 64 query heads per item (group = heads per group)
 };
 
 struct MergeParams {
@@ -94,7 +94,8 @@ struct BalancedMergeParams {
   const int32_t* sched;         // U, total, -, -, S_0 .. S_B (written by the attention kernel)
   int32_t num_seqs;
   int32_t num_q_heads;
-  int32_t num_kv_heads;
+  int32_t num_kv_heads;         // items per sequence (KV heads, or MLA head groups)
+  int32_t rows_per_item;        // query rows of one item (G, or MLA heads per group)
   int32_t max_total_q;
   const int32_t* cu_q_lens;     // NULL: token b = sequence b
   uint16_t* out;

@@ -1211,12 +1211,17 @@ __device__ __forceinline__ int seq_units(const AttnParams& p, int b) {
   return (qn > 0 && L > 0) ? (L + kUnitKeys - 1) >> kUnitShift : 0;
 }
 
-template <int D, bool FP8, int MODE>
-__device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pcache, int* meta) {
-  constexpr int NTH = Block<MODE, D>::threads;
+// Balanced schedule prologue: the unit scan (block-wide prefix sum of
+// seq_units over the batch, NTH threads), this workgroup's units [u0, u1)
+// with U = ceil(total / grid) and the sequence b holding u0 with its unit
+// offset S_b; workgroup 0 publishes U, the total and every S_b in p.sched.
+// `per_seq` is the number of items per sequence (KV heads, or MLA head
+// groups).  Returns false when the workgroup has no units.
+template <int NTH>
+__device__ bool balanced_start(const AttnParams& p, uint8_t* smem, int* meta, int per_seq, int& u0, int& u1,
+                               int& b, int& S) {
   const int tid = threadIdx.x;
   const int B = p.num_seqs;
-  const int Hkv = p.num_kv_heads;
   // units per thread chunk of sequences, then an exclusive scan over threads
   const int per = (B + NTH - 1) / NTH;
   const int j0 = min(B, tid * per), j1 = min(B, j0 + per);
@@ -1232,12 +1237,12 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
     __syncthreads();
   }
   const int excl = scan[tid] - mine;           // sequence units before this chunk
-  const int total = scan[NTH - 1] * Hkv;       // item units in the whole batch
+  const int total = scan[NTH - 1] * per_seq;   // item units in the whole batch
   const int W = gridDim.x;
   const int U = (total + W - 1) / max(W, 1);
   const int w = blockIdx.x;
-  const int u0 = min(total, w * U);
-  const int u1 = min(total, u0 + U);
+  u0 = min(total, w * U);
+  u1 = min(total, u0 + U);
   if (w == 0) {
     if (tid == 0) {
       p.sched[0] = U;
@@ -1251,11 +1256,11 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
     if (tid == NTH - 1) p.sched[4 + B] = acc;
   }
   // the sequence holding unit u0
-  if (u0 < u1 && Hkv * excl <= u0 && u0 < Hkv * (excl + mine)) {
+  if (u0 < u1 && per_seq * excl <= u0 && u0 < per_seq * (excl + mine)) {
     int acc = excl;
     for (int j = j0; j < j1; ++j) {
       const int sj = seq_units(p, j);
-      if (u0 < Hkv * (acc + sj)) {
+      if (u0 < per_seq * (acc + sj)) {
         meta[0] = j;
         meta[1] = acc;
         break;
@@ -1264,9 +1269,18 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
     }
   }
   __syncthreads();
-  if (u0 >= u1) return;
-  int b = __builtin_amdgcn_readfirstlane(meta[0]);
-  int S = __builtin_amdgcn_readfirstlane(meta[1]);
+  if (u0 >= u1) return false;
+  b = __builtin_amdgcn_readfirstlane(meta[0]);
+  S = __builtin_amdgcn_readfirstlane(meta[1]);
+  return true;
+}
+
+template <int D, bool FP8, int MODE>
+__device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pcache, int* meta) {
+  const int Hkv = p.num_kv_heads;
+  const int w = blockIdx.x;
+  int u0, u1, b, S;
+  if (!balanced_start<Block<MODE, D>::threads>(p, smem, meta, Hkv, u0, u1, b, S)) return;
   float c, vdesc;
   score_scales<FP8>(p, c, vdesc);
   int u = u0;
@@ -1627,43 +1641,15 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
   }
 }
 
-// Item = (sequence b, split window, head group of up to 64 query heads), NCT
-// 32-row tiles of query heads.  The four waves split the work by columns:
-// wave w contracts columns [144 w, 144 w + 144) of q.C for every row tile
-// (its 36 query values per row in registers), the partial scores are summed
-// through LDS so that every wave holds the same full scores, the softmax is
-// split four ways (mla_keys), and wave w accumulates the value columns
-// [128 w, 128 w + 128).  No product is computed twice.  More than 64 heads
-// take several head groups (their score and accumulator registers would not
-// fit one wave).  The grid is one-dimensional; items are ordered (b, split,
-// group) and dealt so that each XCD takes a contiguous run of them, which puts
-// the head groups of one window on one L2.
+// One MLA item: the keys [klo, khi) of sequence b for head group hg, then its
+// outputs -- final rows (slot < 0), a split-KV partial record (split
+// schedule) or a balanced partial record in slot `slot`.
 template <int NCT>
-__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_kernel(AttnParams p) {
+__device__ void mla_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int hg, int L, int klo,
+                         int khi, int slot, int wave, int lane) {
   using LD = MlaLds<NCT>;
   constexpr int QJ = kMlaDk / 16 / kDecWaves;
   constexpr int VT = kMlaLatent / 32 / kDecWaves;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
-  int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int hg, b, split;
-  {
-    const int n = gridDim.x;
-    const int lin = blockIdx.x;
-    const int full = n - n % kXcds;
-    const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
-    hg = logical % p.head_groups;
-    const int rest = logical / p.head_groups;
-    split = rest % p.num_splits;
-    b = rest / p.num_splits;
-  }
-  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
-  const int klo = split * p.split_keys;
-  // the last window takes every remaining key
-  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
-
   // this wave's query columns of every row tile
   bf16x8 qreg[NCT][QJ];
 #pragma unroll
@@ -1707,8 +1693,10 @@ void mla_kernel(AttnParams p) {
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : vdesc / l_tot;
     const float lse2 = empty ? neg_inf() : st[rt].m + __builtin_amdgcn_logf(l_tot);
-    if (p.num_splits > 1) {
-      const int64_t row = ((int64_t)split * p.max_total_q + b) * p.num_q_heads + h;
+    if (slot >= 0) {
+      // balanced records hold the group's rows (p.group of them) per slot
+      const int64_t row = p.balanced ? (int64_t)slot * p.group + (h - hg * NCT * kCols)
+                                     : ((int64_t)slot * p.max_total_q + b) * p.num_q_heads + h;
       if (wave == 0 && (lane >> 5) == 0) p.part_lse[row] = lse2;
       if (empty) continue;
       float* dst = p.part_o + row * kMlaLatent + d_base;
@@ -1736,6 +1724,78 @@ void mla_kernel(AttnParams p) {
       if (p.lse && wave == 0 && (lane >> 5) == 0) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
     }
   }
+}
+
+// MLA decode.  Item = (sequence b, key window, head group of up to 64 query
+// heads), NCT 32-row tiles of query heads.  The four waves split the work by
+// columns: wave w contracts columns [144 w, 144 w + 144) of q.C for every row
+// tile (its 36 query values per row in registers), the partial scores are
+// summed through LDS so that every wave holds the same full scores, the
+// softmax is split four ways (mla_keys), and wave w accumulates the value
+// columns [128 w, 128 w + 128).  No product is computed twice.  More than 64
+// heads take several head groups (their score and accumulator registers
+// would not fit one wave).
+//   Split schedule: one workgroup per (b, window, group); items are ordered
+//   (b, split, group) and dealt so that each XCD takes a contiguous run of
+//   them, which puts the head groups of one window on one L2.
+//   Balanced schedule (p.balanced): one workgroup per compute unit, each
+//   taking an equal run of 128-key units over all (b, group) items laid end
+//   to end (balanced_start), piece by piece; cut pieces become partial
+//   records for merge_balanced_kernel.
+template <int NCT>
+__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_kernel(AttnParams p) {
+  using LD = MlaLds<NCT>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
+  int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
+  int* meta = reinterpret_cast<int*>(smem + LD::pcache_off - 64);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (p.balanced) {
+    const int HG = p.head_groups;
+    const int w = blockIdx.x;
+    int u0, u1, b, S;
+    if (!balanced_start<kDecWaves * kWave>(p, smem, meta, HG, u0, u1, b, S)) return;
+    int u = u0;
+    int piece = 0;
+    while (u < u1) {
+      const int sb = seq_units(p, b);
+      const int item0 = HG * S;
+      if (sb == 0 || u >= item0 + HG * sb) {    // past this sequence's items
+        S += sb;
+        ++b;
+        continue;
+      }
+      const int hg = (u - item0) / sb;
+      const int a0 = item0 + hg * sb;
+      const int a1 = a0 + sb;
+      const int pu1 = min(u1, a1);
+      const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+      const int klo = (u - a0) << kUnitShift;
+      const int khi = min(L, (pu1 - a0) << kUnitShift);
+      const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
+      mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, slot, wave, lane);
+      u = pu1;
+      ++piece;
+    }
+    return;
+  }
+  int hg, b, split;
+  {
+    const int n = gridDim.x;
+    const int lin = blockIdx.x;
+    const int full = n - n % kXcds;
+    const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
+    hg = logical % p.head_groups;
+    const int rest = logical / p.head_groups;
+    split = rest % p.num_splits;
+    b = rest / p.num_splits;
+  }
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  const int klo = split * p.split_keys;
+  // the last window takes every remaining key
+  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
+  mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1795,7 +1855,7 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedMergeParams
   if (qn <= 0) return;
   const int t = p.cu_q_lens ? p.cu_q_lens[b] : b;
   if (t >= p.max_total_q) return;
-  const int G = p.num_q_heads / p.num_kv_heads;
+  const int G = p.rows_per_item;
   const int g = h / G, r = h - g * G;
   const int U = p.sched[0];
   const int S = p.sched[4 + b];
@@ -2075,6 +2135,7 @@ hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hip
     case 64: hipLaunchKernelGGL(merge_balanced_kernel<64>, grid, dim3(256), 0, stream, p); break;
     case 128: hipLaunchKernelGGL(merge_balanced_kernel<128>, grid, dim3(256), 0, stream, p); break;
     case 256: hipLaunchKernelGGL(merge_balanced_kernel<256>, grid, dim3(256), 0, stream, p); break;
+    case 512: hipLaunchKernelGGL(merge_balanced_kernel<512>, grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -64,6 +64,10 @@ def test_mla_random(seed):
     r = ref(w)
     for s in (0, 1, 3):
         run_check(w, num_splits=s, r=r)
+    # balanced schedule on the device's grid and on tiny grids (items cut
+    # into many pieces across workgroups)
+    for cus in (0, 1, 3, 7):
+        run_check(w, num_splits=-1, num_cus=cus, r=r)
 
 
 def test_mla_long_sequence_many_splits():
@@ -72,6 +76,8 @@ def test_mla_long_sequence_many_splits():
     r = ref(w)
     run_check(w, r=r)
     run_check(w, num_splits=7, r=r)
+    run_check(w, num_splits=-1, r=r)
+    run_check(w, num_splits=-1, num_cus=5, r=r)
 
 
 @pytest.mark.slow
@@ -82,3 +88,4 @@ def test_mla_full_size(make):
     rows = sorted(set(int(b) * w.num_q_heads + int(h) for b, h in
                       zip(rng.integers(0, w.num_seqs, 96), rng.integers(0, w.num_q_heads, 96))))
     run_check(w, rows=rows)
+    run_check(w, rows=rows, num_splits=-1)

@@ -214,11 +214,17 @@ def test_mla_plan():
     p = B.pa_mla_plan(mdesc(num_q_heads=128))
     assert B.pa_mla_num_splits(p) == 2
     B.pa_mla_plan_destroy(p)
+    # balanced on request: one workgroup per CU, two records of the group's rows each
+    p = B.pa_mla_plan(mdesc(num_splits=-1, num_q_heads=100))
+    assert B.pa_mla_num_splits(p) == -1
+    assert B.pa_mla_workspace_bytes(p) >= 2 * 256 * 64 * (512 + 1) * 4 + (4 + 64 + 1) * 4
+    B.pa_mla_plan_destroy(p)
     # many sequences: no split, no workspace
     p = B.pa_mla_plan(mdesc(num_seqs=512))
     assert B.pa_mla_num_splits(p) == 1 and B.pa_mla_workspace_bytes(p) == 0
     B.pa_mla_plan_destroy(p)
     for bad, code in ((dict(num_q_heads=129), B.PA_ERR_UNSUPPORTED), (dict(page_size=8), B.PA_ERR_UNSUPPORTED),
+                      (dict(num_splits=-2), B.PA_ERR_INVALID),
                       (dict(num_q_heads=0), B.PA_ERR_INVALID), (dict(max_seq_len=5000), B.PA_ERR_INVALID),
                       (dict(kv_page_stride=100), B.PA_ERR_INVALID)):
         with pytest.raises(B.PaError) as e:
