@@ -1,4 +1,5 @@
-"""GPU behaviour around the kernels: HIP-graph capture with metadata mutated in
+"""GPU behaviour around the kernels: HIP-graph capture (split, balanced and MLA
+decode, mixed runs, the KV append) with metadata or contents mutated in
 place between replays, workspace reuse across calls and plans, a row-strided
 page table whose padding columns name the poison page, empty sequences, and
 non-causal runs."""
@@ -153,3 +154,104 @@ def test_long_window_crosses_page_cache_chunks():
         out, lse = pa.run(mode, xq)
         torch.cuda.synchronize()
         check(wq, out, lse, *refq, rows=rows, what="longq/" + mode)
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_replay_balanced_decode():
+    # the balanced schedule rewrites its unit offsets in the workspace on
+    # every run; replays with other lengths must see them refreshed
+    wa, wb = twin_workloads(17, decode=True)
+    x = DeviceInputs(wa)
+    pa = PagedAttention(wa, num_splits=-1, num_cus=37,
+                        max_seq_len=max(wa.max_seq_len, wb.max_seq_len))
+    assert pa.info.balanced_workgroups == 37 * 2
+    out, lse = pa.new_outputs(x)
+    refs = [H.run_oracle(wa), H.run_oracle(wb)]
+    pa.run("decode", x, out=out, lse=lse)
+    torch.cuda.synchronize()
+    check(wa, out, lse, *refs[0], what="balanced eager")
+    g = _capture(lambda: pa.run("decode", x, out=out, lse=lse))
+    for rep in range(4):
+        w = (wa, wb)[rep % 2]
+        for dst, src in ((x.q, w.q), (x.k_pool, w.k_pool), (x.v_pool, w.v_pool),
+                         (x.page_table, w.page_table), (x.seq_lens, w.seq_lens)):
+            dst.copy_(src)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(w, out, lse, *refs[rep % 2], what="balanced replay %d" % rep)
+
+
+def test_graph_replay_mla():
+    import dataclasses
+    import oracle
+    from paged_kv_gqa_attention_amd.attention import MlaDecode
+    wa = synth.build_mla(name="mla_graph", seq_lens=[700, 90, 1300, 33], num_q_heads=64, page_size=32,
+                         seed=41, threads=2)
+    qb = synth.normal_bf16(wa.q.numel(), 42, 2, 2).view(wa.q.shape)
+    wb = dataclasses.replace(wa, q=qb, seq_lens=torch.tensor([650, 1, 1290, 20], dtype=torch.int32))
+    m = MlaDecode(wa, num_splits=3)
+    out, lse = m.new_outputs()
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def ref(w):
+        return oracle.mla_decode(q_bits=bits(w.q), kv_cache=bits(w.kv), page_table=w.page_table.numpy(),
+                                 seq_lens=w.seq_lens.numpy(), num_q_heads=w.num_q_heads,
+                                 page_size=w.page_size, scale=w.scale, pt_cols=w.pt_cols)
+    refs = [ref(wa), ref(wb)]
+    g = _capture(lambda: m.run(out, lse))
+    for rep in range(4):
+        w = (wa, wb)[rep % 2]
+        m.q.copy_(w.q)
+        m.seq_lens.copy_(w.seq_lens)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        l = lse.cpu().numpy()
+        ro, rl = refs[rep % 2]
+        assert np.all(np.isfinite(o))
+        assert np.max(np.abs(o - ro)) <= 1.5e-2 and np.max(np.abs(l - rl)) <= 1e-3, "mla replay %d" % rep
+
+
+def test_graph_replay_append():
+    import oracle
+    w = H.random_workload(77, kv_dtype="fp8_e4m3", B=4, max_len=200)
+    x = DeviceInputs(w)
+    pa = PagedAttention(w)
+    T, Hkv, D = w.total_q, w.num_kv_heads, w.head_dim
+    k_new = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v_new = torch.empty_like(k_new)
+    a = B.make_append_args(k_new=k_new, v_new=v_new, cu_new=x.cu_q_lens, seq_lens=x.seq_lens,
+                           page_table=x.page_table, k_pool=x.k_pool, v_pool=x.v_pool,
+                           k_descale=x.k_descale, v_descale=x.v_descale)
+    g = _capture(lambda: B.pa_run_append(pa.plan, a, B.current_stream()))
+    kp, vp = w.k_pool.numpy().copy(), w.v_pool.numpy().copy()
+    for rep in range(3):
+        kn = synth.normal_bf16(T * Hkv * D, 90 + rep, 1, 1).view(T, Hkv, D)
+        vn = synth.normal_bf16(T * Hkv * D, 90 + rep, 2, 1).view(T, Hkv, D)
+        k_new.copy_(kn)
+        v_new.copy_(vn)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        kp, vp = oracle.append(k_new=kn.view(torch.int16).numpy().view(np.uint16),
+                               v_new=vn.view(torch.int16).numpy().view(np.uint16), k_pool=kp, v_pool=vp,
+                               page_table=w.page_table.numpy(), cu_new=w.cu_q_lens.numpy(),
+                               seq_lens=w.seq_lens.numpy(), num_kv_heads=Hkv, head_dim=D,
+                               page_size=w.page_size, kv_dtype=oracle.KV_FP8_E4M3,
+                               k_descale=w.k_descale, v_descale=w.v_descale, pt_cols=w.pt_cols)
+        assert np.array_equal(x.k_pool.cpu().numpy(), kp) and np.array_equal(x.v_pool.cpu().numpy(), vp), \
+            "append replay %d" % rep
