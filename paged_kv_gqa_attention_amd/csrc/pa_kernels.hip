@@ -1496,10 +1496,13 @@ template <int NCT>
 struct MlaLds {
   static constexpr int xbuf_bytes = kDecWaves * NCT * 4 * kWave * 16;   // partial scores
   static constexpr int pbuf_bytes = NCT * 2 * kWave * 16;               // bf16 probabilities
-  static constexpr int ring = (kLdsMax - 64 - kPcacheEntries * 4 - xbuf_bytes - pbuf_bytes) / MlaGeo::tile_bytes;
+  static constexpr int mbuf_bytes = NCT * kWave * 16;                   // per-wave row maxima
+  static constexpr int ring = (kLdsMax - 64 - kPcacheEntries * 4 - xbuf_bytes - pbuf_bytes - mbuf_bytes) /
+                              MlaGeo::tile_bytes;
   static constexpr int xbuf_off = ring * MlaGeo::tile_bytes;
   static constexpr int pbuf_off = xbuf_off + xbuf_bytes;
-  static constexpr int pcache_off = pbuf_off + pbuf_bytes + 64;
+  static constexpr int mbuf_off = pbuf_off + pbuf_bytes;
+  static constexpr int pcache_off = mbuf_off + mbuf_bytes + 64;
   static constexpr int bytes = pcache_off + kPcacheEntries * 4;
   static_assert(ring >= 2 && bytes <= kLdsMax, "MLA LDS budget exceeded");
 };
@@ -1523,6 +1526,7 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
   constexpr int VT = kMlaLatent / 32 / kDecWaves;   // value tiles per wave
   uint8_t* xbuf = smem + LD::xbuf_off;
   uint8_t* pbuf = smem + LD::pbuf_off;
+  uint8_t* mbuf = smem + LD::mbuf_off;
   PageWalk w;
   w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
   w.page_bytes = p.kv_page_bytes;
@@ -1551,8 +1555,6 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
       else
         wait_vmem<0>();
       ring_barrier();
-      if (t + R - 1 < ntiles)
-        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
       const uint8_t* kl = smem + (t % R) * MlaGeo::tile_bytes;
       // partial scores over this wave's columns
       f32x16 s[NCT];
@@ -1566,8 +1568,13 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
 #pragma unroll
         for (int rt = 0; rt < NCT; ++rt) s[rt] = mfma32(a, qreg[rt][jj], s[rt]);
       }
-      // exchange: 16-byte records [wave][row tile][quarter][lane]; every wave
-      // sums the four partials in the same order, so all hold identical scores
+      // the next loads are issued while the score MFMAs run (the buffer they
+      // fill was last read in the previous iteration, before the barrier)
+      if (t + R - 1 < ntiles)
+        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
+      // reduce-scatter of the partial scores: 16-byte records
+      // [source wave][row tile][quarter][lane]; wave w sums quarter w (elements
+      // 4 w .. 4 w + 3 of every lane) over the four sources in a fixed order
 #pragma unroll
       for (int rt = 0; rt < NCT; ++rt)
 #pragma unroll
@@ -1575,38 +1582,34 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
           *reinterpret_cast<f32x4*>(xbuf + (((wave * NCT + rt) * 4 + q4) * kWave + lane) * 16) =
               f32x4{s[rt][4 * q4], s[rt][4 * q4 + 1], s[rt][4 * q4 + 2], s[rt][4 * q4 + 3]};
       ring_barrier();
-      f32x16 sf[NCT];
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sf[rt][i] = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) {
-#pragma unroll
-        for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(xbuf + (((w2 * NCT + rt) * 4 + q4) * kWave + lane) * 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sf[rt][4 * q4 + e] += v[e];
-          }
-        if (NCT > 1) __builtin_amdgcn_sched_barrier(0);
-      }
       const int k0 = cb + t * kSub;
-      // Softmax split over the waves: all of them form the row max (identical
-      // scores give identical running state), each forms the probabilities of
-      // its quarter of the tile (accumulator elements 4 wave .. 4 wave + 3 of
-      // every lane) and keeps its own partial row sum; the bf16 probabilities
-      // meet in LDS as the PV operand.
+      f32x4 g4[NCT];
 #pragma unroll
       for (int rt = 0; rt < NCT; ++rt) {
-        if (k0 + kSub > khi) mask_tile(sf[rt], k0, khi, lane);
-        float mx = neg_inf();
+        g4[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sf[rt][i], sf[rt][i + 1]));
+        for (int w2 = 0; w2 < kDecWaves; ++w2)
+          g4[rt] += *reinterpret_cast<const f32x4*>(xbuf + (((w2 * NCT + rt) * 4 + wave) * kWave + lane) * 16);
+        // this quarter's keys past the window are masked; soft cap if asked
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = g4[rt][e];
+          if constexpr (CAP) v = cap1(v, sc);
+          g4[rt][e] = k0 + acc_key(4 * wave + e, lane) < khi ? v : neg_inf();
+        }
+        // this wave's part of the row maximum (both lane halves hold the row)
+        float mx = fmaxf(fmaxf(g4[rt][0], g4[rt][1]), fmaxf(g4[rt][2], g4[rt][3]));
         mx = fmaxf(mx, xor32(mx));
-        float mxs = mx * c;
-        if constexpr (CAP) mxs = mx == neg_inf() ? neg_inf() : cap1(mx, sc) * c;   // tanh is monotonic
+        reinterpret_cast<float*>(mbuf)[(rt * kWave + lane) * 4 + wave] = mx;
+      }
+      ring_barrier();
+      // Softmax split over the waves: every wave forms the same row maximum
+      // and running state, the probabilities of its quarter and its own
+      // partial row sum; the bf16 probabilities meet in LDS as the PV operand.
+#pragma unroll
+      for (int rt = 0; rt < NCT; ++rt) {
+        const f32x4 m4 = *reinterpret_cast<const f32x4*>(mbuf + (rt * kWave + lane) * 16);
+        const float mxs = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c;
         if (__builtin_amdgcn_ballot_w64(mxs > st[rt].m + kRescaleSlack)) {
           const float m_new = fmaxf(st[rt].m, mxs);
           const float alpha = __builtin_amdgcn_exp2f(st[rt].m - (m_new == neg_inf() ? 0.f : m_new));
@@ -1620,12 +1623,7 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
         const float nref = st[rt].m == neg_inf() ? 0.f : -st[rt].m;
         float pq[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // element 4 wave + e, picked with wave-uniform selects
-          float v = wave == 0 ? sf[rt][e] : wave == 1 ? sf[rt][4 + e] : wave == 2 ? sf[rt][8 + e] : sf[rt][12 + e];
-          if constexpr (CAP) v = v == neg_inf() ? neg_inf() : cap1(v, sc);
-          pq[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(v, c, nref));
-        }
+        for (int e = 0; e < 4; ++e) pq[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(g4[rt][e], c, nref));
         st[rt].l += (pq[0] + pq[1]) + (pq[2] + pq[3]);
         *reinterpret_cast<u32x2*>(pbuf + ((rt * 2 + (wave >> 1)) * kWave + lane) * 16 + (wave & 1) * 8) =
             u32x2{pack_bf16x2(pq[0], pq[1]), pack_bf16x2(pq[2], pq[3])};
