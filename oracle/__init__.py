@@ -25,6 +25,8 @@ _LIB = os.path.join(_HERE, "libpa_oracle.so")
 
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+Q_BF16 = 0
+Q_FP8_E4M3 = 1
 
 
 def compile_source(src: str, out: str) -> str:
@@ -62,6 +64,8 @@ class Problem(ctypes.Structure):
         ("k_descale", ctypes.c_double),
         ("v_descale", ctypes.c_double),
         ("softcap", ctypes.c_double),
+        ("q_dtype", ctypes.c_int32),
+        ("q_descale", ctypes.c_double),
     ]
 
 
@@ -146,11 +150,13 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
               rows: Optional[Sequence[int]] = None,
               key_begin: int = 0, key_end: int = -1,
               q_stride_t: int = 0, kv_page_stride: int = 0,
-              pt_cols: Optional[int] = None, threads: int = 0, softcap: float = 0.0):
+              pt_cols: Optional[int] = None, threads: int = 0, softcap: float = 0.0,
+              q_dtype: int = Q_BF16, q_descale: float = 1.0):
     """Reference attention in fp64.
 
     q_bits   : uint16 bf16 bit patterns, [T, Hq, D] (or a flat buffer with
-               ``q_stride_t`` elements between tokens)
+               ``q_stride_t`` elements between tokens); uint8 E4M3 codes when
+               ``q_dtype`` is Q_FP8_E4M3 (value = code * q_descale)
     k_pool, v_pool : uint16 (bf16 bits) or uint8 (fp8 e4m3 bytes),
                [P, page, Hkv, D] (or flat with ``kv_page_stride``)
     page_table : int32 [B, row_stride]; the first ``pt_cols`` columns (default:
@@ -164,7 +170,7 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         raise OracleError("page_table must be 2-D [B, row_stride]")
     cu_q_lens = _c(cu_q_lens, np.int32)
     seq_lens = _c(seq_lens, np.int32)
-    q_bits = _c(q_bits, np.uint16)
+    q_bits = _c(q_bits, np.uint16 if q_dtype == Q_BF16 else np.uint8)
     kv_np = np.uint16 if kv_dtype == KV_BF16 else np.uint8
     k_pool = _c(k_pool, kv_np)
     v_pool = _c(v_pool, kv_np)
@@ -178,7 +184,8 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                  pt_row_stride=page_table.shape[1],
                  kv_page_stride=kv_page_stride, q_stride_t=q_stride_t,
                  kv_dtype=kv_dtype, causal=1 if causal else 0, scale=scale,
-                 k_descale=k_descale, v_descale=v_descale, softcap=softcap)
+                 k_descale=k_descale, v_descale=v_descale, softcap=softcap,
+                 q_dtype=q_dtype, q_descale=q_descale)
     T = int(cu_q_lens[B]) if B else 0
     if rows is None:
         rows_arr = None

@@ -65,6 +65,8 @@ static int check_problem(const pao_problem* pr) {
   if (pr->kv_dtype != PAO_KV_BF16 && pr->kv_dtype != PAO_KV_FP8_E4M3)
     return PAO_ERR_ARG;
   if (!(pr->softcap >= 0.0) || isinf(pr->softcap)) return PAO_ERR_ARG;
+  if (pr->q_dtype != PAO_Q_BF16 && pr->q_dtype != PAO_Q_FP8_E4M3) return PAO_ERR_ARG;
+  if (pr->head_dim > 1024) return PAO_ERR_ARG;
   return PAO_OK;
 }
 
@@ -87,7 +89,7 @@ static int check_metadata(const pao_problem* pr, const int32_t* page_table,
 }
 
 /* One output row (t, h): gather keys through the page table, two-pass softmax. */
-static void one_row(const pao_problem* pr, const uint16_t* q,
+static void one_row(const pao_problem* pr, const void* q,
                     const void* k_pool, const void* v_pool,
                     const int32_t* page_table, const int32_t* cu_q_lens,
                     const int32_t* seq_lens, int32_t key_begin, int32_t key_end,
@@ -122,15 +124,21 @@ static void one_row(const pao_problem* pr, const uint16_t* q,
     return;
   }
 
-  const uint16_t* qrow = q + t * q_stride + h * D;
+  /* The query row, decoded: bf16 exactly, or (fp8 queries, the fp8-in path
+   * of vLLM PR #48156, fp8/descale discussion: fp8 inputs, bf16 output)
+   * e4m3(byte) * q_descale. */
+  double qrow[1024];
+  for (int64_t d = 0; d < D; ++d)
+    qrow[d] = pr->q_dtype == PAO_Q_FP8_E4M3
+                  ? pao_fp8_e4m3_to_double(((const uint8_t*)q)[t * q_stride + h * D + d]) * pr->q_descale
+                  : pao_bf16_to_double(((const uint16_t*)q)[t * q_stride + h * D + d]);
   double m = -INFINITY;
   for (int64_t j = lo; j < hi; ++j) {
     const int64_t phys = page_table[b * pr->pt_row_stride + j / pr->page_size];
     const int64_t slot = j % pr->page_size;
     double dot = 0.0;
     for (int64_t d = 0; d < D; ++d)
-      dot += pao_bf16_to_double(qrow[d]) *
-             kv_elem(pr, k_pool, phys, slot, g, d, pr->k_descale);
+      dot += qrow[d] * kv_elem(pr, k_pool, phys, slot, g, d, pr->k_descale);
     s[j - lo] = pr->scale * dot;
     /* Logit soft-capping: the unified kernel of vLLM PR #16828 (review thread
      * on the masked-score line) caps the scaled scores before the mask; the
@@ -152,7 +160,7 @@ static void one_row(const pao_problem* pr, const uint16_t* q,
   *lse_out = lse;
 }
 
-int pao_attention(const pao_problem* pr, const uint16_t* q, const void* k_pool,
+int pao_attention(const pao_problem* pr, const void* q, const void* k_pool,
                   const void* v_pool, const int32_t* page_table,
                   const int32_t* cu_q_lens, const int32_t* seq_lens,
                   int32_t key_begin, int32_t key_end, const int64_t* rows,

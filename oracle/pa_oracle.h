@@ -53,6 +53,7 @@ extern "C" {
 
 enum { PAO_OK = 0, PAO_ERR_ARG = -1, PAO_ERR_DATA = -2 };
 enum { PAO_KV_BF16 = 0, PAO_KV_FP8_E4M3 = 1 };
+enum { PAO_Q_BF16 = 0, PAO_Q_FP8_E4M3 = 1 };
 
 typedef struct {
   int32_t num_seqs;        /* B */
@@ -71,6 +72,9 @@ typedef struct {
   double k_descale;        /* fp8 only: K value = e4m3(byte) * k_descale */
   double v_descale;        /* fp8 only: V value = e4m3(byte) * v_descale */
   double softcap;          /* > 0: scores s -> softcap * tanh(s / softcap); 0: off */
+  int32_t q_dtype;         /* PAO_Q_BF16, or PAO_Q_FP8_E4M3: q holds E4M3 codes and
+                              the query value is e4m3(byte) * q_descale */
+  double q_descale;
 } pao_problem;
 
 /* Exact decoders of the element formats. */
@@ -79,7 +83,8 @@ double pao_fp8_e4m3_to_double(uint8_t byte);
 
 /*
  * Reference attention.
- *   q          : bf16 bits, token t / head h / dim d at q[t*q_stride_t + h*D + d]
+ *   q          : bf16 bits (or E4M3 bytes, q_dtype), token t / head h / dim d at
+ *                q[t*q_stride_t + h*D + d]
  *   k_pool, v_pool : uint16 (bf16) or uint8 (fp8) elements, [P][page][Hkv][D]
  *                with kv_page_stride between pages
  *   page_table : int32 [B][pt_row_stride]; only the first ceil(L_b/page)
@@ -96,7 +101,7 @@ double pao_fp8_e4m3_to_double(uint8_t byte);
  * row index outside [0, T*Hq)).
  */
 int pao_attention(const pao_problem* pr,
-                  const uint16_t* q,
+                  const void* q,
                   const void* k_pool, const void* v_pool,
                   const int32_t* page_table,
                   const int32_t* cu_q_lens, const int32_t* seq_lens,

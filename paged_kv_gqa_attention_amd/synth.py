@@ -59,6 +59,8 @@ class Workload:
     v_descale: float = 1.0
     poison_page: int = -1
     softcap: float = 0.0         # > 0: scores s -> softcap * tanh(s / softcap)
+    q_dtype: str = "bf16"        # or "fp8_e4m3": q holds E4M3 codes (uint8), value = code * q_descale
+    q_descale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -169,7 +171,7 @@ def build(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
           seed: int, kv_dtype: str = "bf16", causal: bool = True,
           scale: Optional[float] = None, pt_cols: Optional[int] = None,
           pt_row_stride: Optional[int] = None, num_pages: Optional[int] = None,
-          poison: bool = True, threads: int = 8) -> Workload:
+          poison: bool = True, threads: int = 8, q_dtype: str = "bf16") -> Workload:
     """Generic builder; every named workload below is a call of this."""
     L = np.asarray(seq_lens, dtype=np.int64)
     ql = np.asarray(q_lens, dtype=np.int64)
@@ -232,6 +234,15 @@ def build(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
     else:
         raise ValueError(kv_dtype)
 
+    q_descale = 1.0
+    if q_dtype == "fp8_e4m3":
+        # the same per-tensor quantisation as the cache: descale = amax / 448
+        amax_q = float(q.abs().max().to(torch.float32)) if q.numel() else 1.0
+        q_descale = float(np.float32(amax_q / 448.0)) if amax_q > 0 else 1.0
+        q = quantize_e4m3(q, q_descale)
+    elif q_dtype != "bf16":
+        raise ValueError(q_dtype)
+
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(ql)
     return Workload(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
@@ -241,7 +252,8 @@ def build(*, name: str, seq_lens: Sequence[int], q_lens: Sequence[int],
                     page_table=torch.from_numpy(pt), pt_cols=int(pt_cols),
                     cu_q_lens=torch.from_numpy(cu),
                     seq_lens=torch.from_numpy(L.astype(np.int32)),
-                    k_descale=k_descale, v_descale=v_descale, poison_page=poison_page)
+                    k_descale=k_descale, v_descale=v_descale, poison_page=poison_page,
+                    q_dtype=q_dtype, q_descale=q_descale)
 
 
 # ---------------------------------------------------------------------------

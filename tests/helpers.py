@@ -15,7 +15,10 @@ from paged_kv_gqa_attention_amd import synth
 
 def bits(w: synth.Workload):
     """numpy views of a workload: q bf16 bits, K/V pools (bf16 bits or fp8 bytes)."""
-    q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if w.q.dtype == torch.uint8:                      # fp8 queries: E4M3 codes
+        q = w.q.contiguous().numpy()
+    else:
+        q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
     if w.kv_dtype == "bf16":
         k = w.k_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
         v = w.v_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
@@ -37,7 +40,9 @@ def run_oracle(w: synth.Workload, rows=None, key_begin=0, key_end=-1, causal=Non
         kv_dtype=oracle.KV_BF16 if w.kv_dtype == "bf16" else oracle.KV_FP8_E4M3,
         k_descale=w.k_descale, v_descale=w.v_descale, rows=rows,
         key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads,
-        softcap=w.softcap if softcap is None else softcap)
+        softcap=w.softcap if softcap is None else softcap,
+        q_dtype=oracle.Q_FP8_E4M3 if w.q_dtype == "fp8_e4m3" else oracle.Q_BF16,
+        q_descale=w.q_descale)
 
 
 def decoded_pools(w: synth.Workload):
@@ -59,6 +64,14 @@ def contiguous_kv(w: synth.Workload, b: int, kpool=None, vpool=None):
     phys = w.page_table[b].to(torch.int64)[j // w.page_size]
     slot = j % w.page_size
     return kpool[phys, slot], vpool[phys, slot]
+
+
+def query_values(w: synth.Workload) -> torch.Tensor:
+    """Queries as float64, decoded with torch's own casts (E4M3 codes times
+    q_descale for fp8 queries)."""
+    if w.q_dtype == "fp8_e4m3":
+        return w.q.view(torch.float8_e4m3fn).to(torch.float64) * w.q_descale
+    return w.q.to(torch.float64)
 
 
 def library_attention(w: synth.Workload, causal=None, scale=None):
@@ -84,7 +97,7 @@ def library_attention(w: synth.Workload, causal=None, scale=None):
         if ql == 0:
             continue
         k, v = contiguous_kv(w, b, kpool, vpool)                   # [L, Hkv, D]
-        qb = w.q[lo:hi].to(torch.float64).permute(1, 0, 2)[None]   # [1, Hq, ql, D]
+        qb = query_values(w)[lo:hi].permute(1, 0, 2)[None]          # [1, Hq, ql, D]
         kb = k.permute(1, 0, 2).repeat_interleave(G, dim=0)[None].contiguous()
         vb = v.permute(1, 0, 2).repeat_interleave(G, dim=0)[None].contiguous()
         if causal and ql == L:
@@ -102,7 +115,7 @@ def library_attention(w: synth.Workload, causal=None, scale=None):
 
 def random_workload(seed: int, *, B=None, D=None, page=None, G=None, Hkv=None,
                     kv_dtype="bf16", causal=True, max_len=80, decode=False,
-                    poison=True) -> synth.Workload:
+                    poison=True, q_dtype="bf16") -> synth.Workload:
     """A small random workload (varying lengths, chunked prefill and decode rows)."""
     rng = np.random.default_rng(seed)
     B = B if B is not None else int(rng.integers(1, 5))
@@ -120,4 +133,4 @@ def random_workload(seed: int, *, B=None, D=None, page=None, G=None, Hkv=None,
     return synth.build(name="random%d" % seed, seq_lens=L, q_lens=ql,
                        num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=page,
                        seed=1000 + seed, kv_dtype=kv_dtype, causal=causal, poison=poison,
-                       threads=1)
+                       threads=1, q_dtype=q_dtype)
