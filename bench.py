@@ -37,6 +37,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-attn prefill TFLOP/s + decode KV GB/s, as % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+FP8_PEAK_TFLOPS = 2 * BF16_PEAK_TFLOPS
+# half the flops at each rate (q.k on fp8, p.v on bf16): 1 / (0.5/fp8 + 0.5/bf16)
+FP8Q_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_attention_amd", "csrc", "pa_kernels.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -95,7 +98,7 @@ def time_steps(fn, steps: int, warmup: int, stream):
 
 
 def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, heads=2,
-                   softcap=0.0, num_splits=0):
+                   softcap=0.0, num_splits=0, kv_dtype=None, q_dtype="bf16"):
     """Generate, time, and (CPU leg) check sampled rows.  Returns a result dict."""
     import torch
     from paged_kv_gqa_attention_amd import binding as B
@@ -103,7 +106,10 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
     from paged_kv_gqa_attention_amd.attention import DeviceInputs, PagedAttention
 
     t0 = time.time()
-    w = synth.WORKLOADS[name]()
+    kw = {} if kv_dtype is None else {"kv_dtype": kv_dtype}
+    if q_dtype != "bf16":
+        kw["q_dtype"] = q_dtype
+    w = synth.WORKLOADS[name](**kw)
     w.softcap = softcap
     gen_s = time.time() - t0
     x = DeviceInputs(w)
@@ -122,8 +128,11 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
     qo = w.qo_bytes()
     flops = w.flops()
     res = {
-        "workload": name + ("_softcap%g" % softcap if softcap else ""), "entry": "pa_run_" + mode,
-        "ms_per_step": ms, "softcap": softcap,
+        "workload": name + ("_softcap%g" % softcap if softcap else "")
+        + ("_fp8kv" if kv_dtype == "fp8_e4m3" and "fp8" not in name else "")
+        + ("_fp8q" if q_dtype == "fp8_e4m3" else ""),
+        "entry": "pa_run_" + mode, "ms_per_step": ms, "softcap": softcap,
+        "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
         "kv_bytes": kv, "qo_bytes": qo, "flops": flops,
         "kv_gbs": kv / (ms * 1e-3) / 1e9,
         "alg_gbs": (kv + qo) / (ms * 1e-3) / 1e9,
@@ -296,6 +305,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default=None, help="time one workload by name and print it")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit soft cap for --only")
+    ap.add_argument("--kv-dtype", default=None, choices=("bf16", "fp8_e4m3"),
+                    help="cache dtype for --only (default: the workload's own)")
+    ap.add_argument("--q-dtype", default="bf16", choices=("bf16", "fp8_e4m3"),
+                    help="query dtype for --only (fp8_e4m3 needs an fp8 cache, prefill)")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="plan num_splits for --only (0 heuristic, -1 balanced decode)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -334,7 +347,8 @@ def main():
             r = bench_mla(a.only, a.steps, a.warmup, cpu_leg, num_splits=a.num_splits)
         else:
             r = bench_workload(a.only, modes[a.only], a.steps, a.warmup, cpu_leg,
-                               softcap=a.softcap, num_splits=a.num_splits)
+                               softcap=a.softcap, num_splits=a.num_splits,
+                               kv_dtype=a.kv_dtype, q_dtype=a.q_dtype)
         print(json.dumps(strip(r)), flush=True)
         return
 
@@ -368,6 +382,20 @@ def main():
         print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
                                                        e["roofline_frac"]),
               file=sys.stderr, flush=True)
+        # fp8 cache, bf16 queries vs fp8 queries: the second runs its score
+        # product on the E4M3 matrix cores (5.0 PFLOP/s dense) and P.V in bf16
+        # (2.5), so its peak is the harmonic mean of the halves, 3.33 PFLOP/s
+        for qd in ("bf16", "fp8_e4m3"):
+            r = bench_workload("prefill_causal", "prefill", max(5, a.steps // 2), a.warmup, cpu_leg,
+                               kv_dtype="fp8_e4m3", q_dtype=qd)
+            e = strip(r)
+            e["bound"] = "mfma"
+            e["peak_tflops"] = FP8Q_PEAK_TFLOPS if qd == "fp8_e4m3" else BF16_PEAK_TFLOPS
+            e["roofline_frac"] = r["tflops"] / e["peak_tflops"]
+            sec[r["workload"]] = e
+            print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
+                                                           e["roofline_frac"]),
+                  file=sys.stderr, flush=True)
         for name in ("mla_decode_h16", "mla_decode_h128"):
             r = bench_mla(name, a.steps, a.warmup, cpu_leg)
             sec[name] = r

@@ -81,6 +81,11 @@ typedef enum {
   PA_KV_FP8_E4M3 = 1        /* K/V pools hold OCP FP8 E4M3 bytes, value = e4m3 * descale */
 } pa_kv_dtype;
 
+typedef enum {
+  PA_Q_BF16 = 0,            /* queries are bfloat16 */
+  PA_Q_FP8_E4M3 = 1         /* queries are OCP FP8 E4M3 bytes, value = e4m3 * q_descale */
+} pa_q_dtype;
+
 /*
  * Shape bounds of a plan (host values only).
  *   num_seqs              B: sequences per run (page-table rows, seq_lens entries)
@@ -110,6 +115,13 @@ typedef enum {
  *                         it would split.
  *   num_cus               compute units to plan for; 0 = query the current device
  *                         (>0 lets plans be built without a GPU)
+ *   q_dtype               PA_Q_BF16, or PA_Q_FP8_E4M3: queries arrive as E4M3
+ *                         codes with a per-tensor q_descale (fp8 inputs, bf16
+ *                         output: the fp8 path of vLLM PR #48156, fp8/descale
+ *                         discussion).  Supported for pa_run_prefill with an
+ *                         fp8 cache and head dim 64 or 128, where the score
+ *                         product runs on the E4M3 matrix cores; other runs of
+ *                         such a plan return PA_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t num_seqs;
@@ -127,6 +139,7 @@ typedef struct {
   int32_t kv_dtype;
   int32_t num_splits;
   int32_t num_cus;
+  int32_t q_dtype;
 } pa_desc;
 
 typedef struct pa_plan_s* pa_plan_t;
@@ -154,6 +167,10 @@ typedef struct pa_plan_s* pa_plan_t;
  *                 visible key get O = 0 and LSE = -inf.
  *   workspace     device scratch of at least pa_workspace_bytes(plan) bytes,
  *                 256-byte aligned; may be NULL when that size is 0
+ *   q_descale     device fp32 scalar, required when the plan's q_dtype is
+ *                 PA_Q_FP8_E4M3 (query value = code * q_descale), else ignored;
+ *                 fp8 queries also need q 16-byte aligned and q_stride_t a
+ *                 multiple of 16
  *   softcap       host float; 0 = off, > 0 = logit soft-capping: each scaled
  *                 score s becomes softcap * tanh(s / softcap) before the mask
  *                 and the softmax (the capped scores of the unified kernel in
@@ -178,6 +195,7 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   float softcap;
+  const float* q_descale;
 } pa_args;
 
 /* What a plan chose (for tests and benchmarks). */

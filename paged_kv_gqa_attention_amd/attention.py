@@ -25,6 +25,8 @@ class DeviceInputs:
         self.cu_q_lens = w.cu_q_lens.to(self.device)
         self.seq_lens = w.seq_lens.to(self.device)
         self.fp8 = w.kv_dtype == "fp8_e4m3"
+        self.q_descale = (torch.tensor([w.q_descale], dtype=torch.float32, device=self.device)
+                          if w.q_dtype == "fp8_e4m3" else None)
         if self.fp8:
             self.k_descale = torch.tensor([w.k_descale], dtype=torch.float32, device=self.device)
             self.v_descale = torch.tensor([w.v_descale], dtype=torch.float32, device=self.device)
@@ -47,7 +49,8 @@ class PagedAttention:
             max_total_q=w.total_q if max_total_q is None else max_total_q,
             max_q_len=w.max_q_len,
             max_seq_len=w.max_seq_len if max_seq_len is None else max_seq_len,
-            kv_dtype=kv, num_splits=num_splits, num_cus=num_cus)
+            kv_dtype=kv, num_splits=num_splits, num_cus=num_cus,
+            q_dtype=B.PA_Q_FP8_E4M3 if w.q_dtype == "fp8_e4m3" else B.PA_Q_BF16)
         self.plan = B.pa_plan(self.desc)
         self.info = B.pa_plan_get_info(self.plan)
         nbytes = B.pa_workspace_bytes(self.plan)
@@ -74,10 +77,11 @@ class PagedAttention:
                            causal=self.w.causal if causal is None else causal,
                            out=out, lse=lse, k_descale=x.k_descale, v_descale=x.v_descale,
                            workspace=self.workspace if workspace is None else workspace,
-                           softcap=self.w.softcap if softcap is None else softcap)
+                           softcap=self.w.softcap if softcap is None else softcap,
+                           q_descale=x.q_descale)
 
     def new_outputs(self, x: DeviceInputs):
-        T, Hq, D = x.q.shape
+        T, Hq, D = x.q.shape                 # bf16 values or E4M3 codes: the same shape
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=self.device)
         lse = torch.empty((T, Hq), dtype=torch.float32, device=self.device)
         return out, lse

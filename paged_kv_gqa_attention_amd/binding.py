@@ -33,6 +33,8 @@ PA_ERR_HIP = -4
 
 PA_KV_BF16 = 0
 PA_KV_FP8_E4M3 = 1
+PA_Q_BF16 = 0
+PA_Q_FP8_E4M3 = 1
 
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
            "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str",
@@ -67,6 +69,7 @@ class pa_desc(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
     ]
 
 
@@ -89,6 +92,7 @@ class pa_args(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("softcap", ctypes.c_float),
+        ("q_descale", ctypes.c_void_p),
     ]
 
 
@@ -259,7 +263,8 @@ def make_desc(*, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: i
               page_size: int, num_pages: int, page_table_cols: int,
               page_table_row_stride: Optional[int] = None, kv_page_stride: int = 0,
               max_total_q: int, max_q_len: int, max_seq_len: int = 0,
-              kv_dtype: int = PA_KV_BF16, num_splits: int = 0, num_cus: int = 0) -> pa_desc:
+              kv_dtype: int = PA_KV_BF16, num_splits: int = 0, num_cus: int = 0,
+              q_dtype: int = PA_Q_BF16) -> pa_desc:
     return pa_desc(num_seqs=num_seqs, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                    head_dim=head_dim, page_size=page_size, num_pages=num_pages,
                    page_table_cols=page_table_cols,
@@ -267,12 +272,13 @@ def make_desc(*, num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: i
                                           is not None else page_table_cols),
                    kv_page_stride=kv_page_stride, max_total_q=max_total_q,
                    max_q_len=max_q_len, max_seq_len=max_seq_len, kv_dtype=kv_dtype,
-                   num_splits=num_splits, num_cus=num_cus)
+                   num_splits=num_splits, num_cus=num_cus, q_dtype=q_dtype)
 
 
 def make_args(*, q, k_pool, v_pool, page_table, cu_q_lens, seq_lens, softmax_scale: float,
               causal: bool, out, lse=None, k_descale=None, v_descale=None, workspace=None,
-              q_stride_t: int = 0, o_stride_t: int = 0, softcap: float = 0.0) -> pa_args:
+              q_stride_t: int = 0, o_stride_t: int = 0, softcap: float = 0.0,
+              q_descale=None) -> pa_args:
     """Build pa_args from device tensors (no copies, no checks beyond the C side)."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return pa_args(q=_ptr(q), q_stride_t=q_stride_t, k_pool=_ptr(k_pool), v_pool=_ptr(v_pool),
@@ -281,7 +287,7 @@ def make_args(*, q, k_pool, v_pool, page_table, cu_q_lens, seq_lens, softmax_sca
                    causal=1 if causal else 0, k_descale=_ptr(k_descale),
                    v_descale=_ptr(v_descale), out=_ptr(out), o_stride_t=o_stride_t,
                    lse=_ptr(lse), workspace=_ptr(workspace), workspace_bytes=ws_bytes,
-                   softcap=float(softcap))
+                   softcap=float(softcap), q_descale=_ptr(q_descale))
 
 
 def make_append_args(*, k_new, v_new, cu_new, seq_lens, page_table, k_pool, v_pool,

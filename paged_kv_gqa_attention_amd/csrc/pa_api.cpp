@@ -72,11 +72,15 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
     return PA_ERR_INVALID;
   if (d.num_q_heads % d.num_kv_heads != 0) return PA_ERR_INVALID;
   if (d.kv_dtype != PA_KV_BF16 && d.kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID;
+  if (d.q_dtype != PA_Q_BF16 && d.q_dtype != PA_Q_FP8_E4M3) return PA_ERR_INVALID;
   const int G = d.num_q_heads / d.num_kv_heads;
   // compiled scope (fail closed)
   if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16 || G == 32)) return PA_ERR_UNSUPPORTED;
   if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (d.page_size != 16 && d.page_size != 32 && d.page_size != 64 && d.page_size != 128)
+    return PA_ERR_UNSUPPORTED;
+  // fp8 queries: the streamed prefill of an fp8 cache (head dim <= 128) only
+  if (d.q_dtype == PA_Q_FP8_E4M3 && (d.kv_dtype != PA_KV_FP8_E4M3 || d.head_dim > 128))
     return PA_ERR_UNSUPPORTED;
   const int esz = d.kv_dtype == PA_KV_FP8_E4M3 ? 1 : 2;
   const int64_t dense_page = (int64_t)d.page_size * d.num_kv_heads * d.head_dim;
@@ -224,6 +228,8 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   if (!plan || !a) return PA_ERR_INVALID;
   const pa_desc& d = plan->d;
   const bool fp8 = d.kv_dtype == PA_KV_FP8_E4M3;
+  const bool q_fp8 = d.q_dtype == PA_Q_FP8_E4M3;
+  if (q_fp8 && mode != pa::kPrefill) return PA_ERR_UNSUPPORTED;
   const int64_t row = (int64_t)d.num_q_heads * d.head_dim;
   const int64_t q_stride = a->q_stride_t ? a->q_stride_t : row;
   const int64_t o_stride = a->o_stride_t ? a->o_stride_t : row;
@@ -234,8 +240,10 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
     if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->out))
       return PA_ERR_INVALID;
     if (fp8 && (!a->k_descale || !a->v_descale)) return PA_ERR_INVALID;
+    if (q_fp8 && !a->q_descale) return PA_ERR_INVALID;
   }
   if (q_stride < row || o_stride < row || q_stride % 8 || o_stride % 8) return PA_ERR_INVALID;
+  if (q_fp8 && q_stride % 16) return PA_ERR_INVALID;      // 16-byte query rows
   // the kernels fold the scale into exp2 arguments and need it positive and finite
   if (!(a->softmax_scale > 0.f) || !(a->softmax_scale < 3.0e38f)) return PA_ERR_INVALID;
   if (!(a->softcap >= 0.f) || !(a->softcap < 3.0e38f)) return PA_ERR_INVALID;
@@ -290,6 +298,8 @@ pa_status prepare(pa_plan_t plan, const pa_args* a, pa::Mode mode, bool use_spli
   p.q_block_tokens = mode == pa::kPrefill ? plan->q_block_tokens : plan->mixed_q_block_tokens;
   p.balanced = balanced ? 1 : 0;
   p.sched = sched;
+  p.q_fp8 = q_fp8 ? 1 : 0;
+  p.q_descale = q_fp8 ? a->q_descale : nullptr;
   return PA_OK;
 }
 

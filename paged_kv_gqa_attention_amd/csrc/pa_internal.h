@@ -19,7 +19,7 @@ namespace pa {
 enum Mode : int { kDecode = 0, kPrefill = 1, kMixed = 2 };
 
 struct AttnParams {
-  const uint16_t* q;            // bf16 bits [T, Hq, D]
+  const uint16_t* q;            // bf16 bits [T, Hq, D] (E4M3 bytes when q_fp8)
   int64_t q_stride_t;           // elements between tokens
   const uint8_t* k_pool;        // raw element bytes
   const uint8_t* v_pool;
@@ -51,6 +51,8 @@ struct AttnParams {
   int32_t balanced;             // decode only: persistent balanced schedule (see launch)
   int32_t* sched;               // balanced: [4 + B + 1] ints of workspace (unit offsets)
   int32_t head_groups;          // MLA: groups of up to 64 query heads per item (group = heads per group)
+  int32_t q_fp8;                // queries are E4M3 codes (streamed fp8 prefill only)
+  const float* q_descale;       // device scalar, fp8 queries
 };
 
 struct MergeParams {

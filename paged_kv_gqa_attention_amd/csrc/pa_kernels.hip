@@ -54,6 +54,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -152,6 +153,13 @@ struct Lds {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x64 product of OCP E4M3 operands (format 0 for both, no block
+// scales): lane l holds row l % 32 and k = 32 (l / 32) .. +31 of its operand
+// (32 bytes); the accumulator layout is that of the bf16 product above.
+__device__ __forceinline__ f32x16 mfma32_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -315,6 +323,16 @@ __device__ __forceinline__ bf16x8 k_operand(const uint8_t* kl, int kb, int j, in
   } else {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(src));
   }
+}
+
+// fp8 K operand for the 64-wide k-step j of the E4M3 score product: the 32
+// bytes K[key = kb + kperm(lane%32)][64 j + 32 (lane/32) .. +32], left in fp8.
+template <int KPITCH>
+__device__ __forceinline__ i32x8 k_operand_f8(const uint8_t* kl, int kb, int j, int lane) {
+  const uint8_t* src = kl + (kb + kperm(lane & 31)) * KPITCH + 64 * j + 32 * (lane >> 5);
+  const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(src + 16);
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -994,28 +1012,53 @@ __device__ __forceinline__ void pv_tile(SoftmaxState<D>& st, const bf16x8 (&pb)[
 // preceded by the LDS read of the operand two MFMAs ahead and followed by its
 // share of the VALU work, so that one wave keeps its matrix core fed while its
 // VALU works through the softmax.
-template <int D, bool FP8, int KPITCH, int VPITCH>
+// Query operands of the streamed schedule: bf16 (16-wide k-steps) or, with
+// fp8 queries, E4M3 (64-wide k-steps of the fp8 product).
+template <bool QF8>
+struct QOp {
+  using reg = bf16x8;
+  template <int D> struct n { static constexpr int value = D / 16; };
+};
+template <>
+struct QOp<true> {
+  using reg = i32x8;
+  template <int D> struct n { static constexpr int value = D / 64; };
+};
+
+template <int D, bool FP8, int KPITCH, int VPITCH, bool QF8>
 __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
                                             const uint8_t* kl, const uint8_t* vl,
-                                            const bf16x8 (&qreg)[D / 16], float c, int lane) {
-  constexpr int NQ = D / 16;            // score MFMAs (k-steps over the head dim)
+                                            const typename QOp<QF8>::reg (&qreg)[QOp<QF8>::template n<D>::value],
+                                            float c, int lane) {
+  constexpr int NQ = QOp<QF8>::template n<D>::value;   // score MFMAs (k-steps over the head dim)
   constexpr int NT = D / 32;            // 32-wide d tiles of O
   constexpr int NV = 2 * NT;            // PV MFMAs; operand v = (tile v % NT, half v / NT)
   constexpr int EPQ = 16 / NQ;          // exps per score MFMA
   const float nref = st.m == neg_inf() ? 0.f : -st.m;
-  bf16x8 ka[NQ];
+  typename QOp<QF8>::reg ka[NQ];
   bf16x8 va[NV];
   float p[16];
+  // operands are fetched two ahead of their MFMA: the K operands of the score
+  // product, then the V operands of the PV product
+  auto fetch = [&](int idx) {
+    if (idx < NQ) {
+      if constexpr (QF8) ka[idx] = k_operand_f8<KPITCH>(kl, 0, idx, lane);
+      else ka[idx] = k_operand<D, FP8, KPITCH>(kl, 0, idx, lane);
+    } else if (idx < NQ + NV) {
+      const int v = idx - NQ;
+      va[v] = v_operand<FP8, VPITCH>(vl, 0, v % NT, v / NT, lane);
+    }
+  };
 #pragma unroll
   for (int i = 0; i < 16; ++i) sn[i] = 0.f;
-  ka[0] = k_operand<D, FP8, KPITCH>(kl, 0, 0, lane);
-  ka[1] = k_operand<D, FP8, KPITCH>(kl, 0, 1, lane);
+  fetch(0);
+  fetch(1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    if (j + 2 < NQ) ka[j + 2] = k_operand<D, FP8, KPITCH>(kl, 0, j + 2, lane);
-    else va[j + 2 - NQ] = v_operand<FP8, VPITCH>(vl, 0, (j + 2 - NQ) % NT, (j + 2 - NQ) / NT, lane);
-    sn = mfma32(ka[j], qreg[j], sn);
+    fetch(j + 2);
+    if constexpr (QF8) sn = mfma32_f8(ka[j], qreg[j], sn);
+    else sn = mfma32(ka[j], qreg[j], sn);
 #pragma unroll
     for (int e = 0; e < EPQ; ++e) {
       const int i = j * EPQ + e;
@@ -1032,7 +1075,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    if (v + 2 < NV) va[v + 2] = v_operand<FP8, VPITCH>(vl, 0, (v + 2) % NT, (v + 2) / NT, lane);
+    fetch(NQ + v + 2);
     st.o[v % NT] = mfma32(va[v], pb[v / NT], st.o[v % NT]);
     if (v == 0) {
 #pragma unroll
@@ -1049,7 +1092,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
 // Within a tile each wave runs 32-key steps; step u issues the score product
 // of step u+1 (K rows of tile t or t+1) before the softmax and PV product of
 // step u, so the two products of a wave overlap its exp work.
-template <int D, bool FP8, int MODE>
+template <int D, bool FP8, int MODE, bool QF8>
 __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                             const PageWalk& pw, int L, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
@@ -1064,17 +1107,31 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   const int r0 = wave * kCols;
   const int last_tok = max(rm.ntok - 1, 0);
 
-  // Q operands of this wave's rows, in registers
-  bf16x8 qreg[D / 16];
+  // Q operands of this wave's rows, in registers (bf16, or E4M3 codes)
+  typename QOp<QF8>::reg qreg[QOp<QF8>::template n<D>::value];
   {
     const int r = r0 + (lane & 31);
     const bool ok = r < nrows;
     const int tok = ok ? r / rm.G : 0;
     const int h = rm.g * rm.G + (r - tok * rm.G);
-    const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
+    if constexpr (QF8) {
+      // the loads are unconditional: a lane past the block's rows reads from
+      // the first query row (head 0 of token 0 always exists), then drops it
+      const int64_t off = ok ? (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D : 0;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.q) + off + 32 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      for (int j = 0; j < D / 64; ++j) {
+        u32x4 a = *reinterpret_cast<const u32x4*>(src + 64 * j);
+        u32x4 b = *reinterpret_cast<const u32x4*>(src + 64 * j + 16);
+        if (!ok) a = b = u32x4{0u, 0u, 0u, 0u};
+        qreg[j] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+      }
+    } else {
+      const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j)
+        qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
   }
 
   int khi = L;
@@ -1135,7 +1192,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
         const uint8_t* kl = smem + (tk % NB) * Gm::tile_bytes + ((u + 1) & 1) * kSub * Gm::k_pitch;
         const uint8_t* vl = smem + (tv % NB) * Gm::tile_bytes + Gm::tile_k_bytes + (u & 1) * kSub * Gm::v_pitch;
         f32x16 sn[1];
-        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch>(st, s_cur, sn[0], kl, vl, qreg, c, lane);
+        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], kl, vl, qreg, c, lane);
         if (u + 1 < nsub) {
           const int k1 = cb + (u + 1) * kSub;
           if (sc.on()) cap_tile(sn[0], sc);
@@ -1311,10 +1368,13 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
   }
 }
 
-template <int D, bool FP8, int MODE>
+// QF8: queries arrive as E4M3 codes (fp8 inputs); only the streamed prefill
+// of an fp8 cache has that variant.
+template <int D, bool FP8, int MODE, bool QF8 = false>
 __global__ __launch_bounds__((Block<MODE, D>::threads))
 __attribute__((amdgpu_waves_per_eu(Block<MODE, D>::waves_per_eu, Block<MODE, D>::waves_per_eu)))
 void attn_kernel(AttnParams p) {
+  static_assert(!QF8 || (FP8 && MODE == kPrefill && Block<MODE, D>::stream), "fp8 queries: streamed fp8 prefill only");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
@@ -1400,7 +1460,7 @@ void attn_kernel(AttnParams p) {
     keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
     if constexpr (Block<MODE, D>::stream)
-      stream_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, c, vdesc);
+      stream_item<D, FP8, MODE, QF8>(p, smem, pcache, rm, pw, L, QF8 ? c * *p.q_descale : c, vdesc);
     else
       rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
   } else {
@@ -2025,6 +2085,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
 template <int D, bool FP8, int MODE>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if constexpr (FP8 && MODE == kPrefill && Block<MODE, D>::stream) {
+    if (p.q_fp8) {
+      hipLaunchKernelGGL((attn_kernel<D, FP8, MODE, true>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.q_fp8) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
   return hipGetLastError();
 }

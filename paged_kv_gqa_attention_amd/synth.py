@@ -115,7 +115,9 @@ class Workload:
         return 4 * self.head_dim * self.visible_pairs()
 
     def qo_bytes(self) -> int:
-        return 2 * self.total_q * self.num_q_heads * self.head_dim * 2
+        """Q read once (1 byte an element for E4M3 codes, else 2) and bf16 O written once."""
+        qe = 1 if self.q_dtype == "fp8_e4m3" else 2
+        return self.total_q * self.num_q_heads * self.head_dim * (qe + 2)
 
 
 def _mix(*xs: int) -> int:

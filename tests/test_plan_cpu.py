@@ -70,6 +70,12 @@ def test_status_strings():
     (dict(num_q_heads=64, num_kv_heads=2, head_dim=256, page_size=128, kv_dtype=B.PA_KV_FP8_E4M3), B.PA_OK),
     (dict(num_q_heads=4, num_kv_heads=4, head_dim=64), B.PA_OK),       # MHA
     (dict(num_seqs=0, max_total_q=0), B.PA_OK),                        # empty batch
+    (dict(q_dtype=B.PA_Q_FP8_E4M3, kv_dtype=B.PA_KV_FP8_E4M3), B.PA_OK),
+    (dict(q_dtype=B.PA_Q_FP8_E4M3, kv_dtype=B.PA_KV_FP8_E4M3, head_dim=64), B.PA_OK),
+    (dict(q_dtype=B.PA_Q_FP8_E4M3), B.PA_ERR_UNSUPPORTED),              # fp8 queries need an fp8 cache
+    (dict(q_dtype=B.PA_Q_FP8_E4M3, kv_dtype=B.PA_KV_FP8_E4M3, head_dim=256, page_size=128),
+     B.PA_ERR_UNSUPPORTED),
+    (dict(q_dtype=5), B.PA_ERR_INVALID),
 ])
 def test_plan_validation(kw, code):
     assert plan_status(**kw) == code
@@ -159,6 +165,17 @@ def test_runs_reject_bad_arguments_without_touching_the_device():
     p = B.pa_plan(desc(kv_dtype=B.PA_KV_FP8_E4M3))
     x = args()
     assert B.lib().pa_run_decode(p, ctypes.byref(x), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
+    # fp8 queries: prefill only, with a q descale and 16-byte query rows
+    p = B.pa_plan(desc(kv_dtype=B.PA_KV_FP8_E4M3, q_dtype=B.PA_Q_FP8_E4M3))
+    x = args()
+    x.k_descale, x.v_descale = 32768, 32772
+    for fn in (B.lib().pa_run_decode, B.lib().pa_run_mixed):
+        assert fn(p, ctypes.byref(x), None) == B.PA_ERR_UNSUPPORTED
+    assert B.lib().pa_run_prefill(p, ctypes.byref(x), None) == B.PA_ERR_INVALID   # no q descale
+    x.q_descale = 32776
+    x.q_stride_t = 32 * 128 + 8
+    assert B.lib().pa_run_prefill(p, ctypes.byref(x), None) == B.PA_ERR_INVALID   # row not 16-byte
     B.pa_plan_destroy(p)
     # a split plan without workspace
     p = B.pa_plan(desc(num_splits=4, page_table_cols=64, max_seq_len=1024))
