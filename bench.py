@@ -139,6 +139,7 @@ def bench_workload(name, mode, steps, warmup, cpu_leg, sample_rows_per_seq=2, he
         "tflops": flops / (ms * 1e-3) / 1e12,
         "num_splits": int(pa.info.num_splits),
         "balanced_workgroups": int(pa.info.balanced_workgroups),
+        "queue_workgroups": int(pa.info.queue_workgroups) if mode == "mixed" else 0,
         "validated_rows": 0, "max_abs_err_o": None, "max_abs_err_lse": None,
         "valid": None, "gen_s": round(gen_s, 2), "w": w,
     }

@@ -109,10 +109,15 @@ typedef enum {
  *                         share of all (sequence, KV head) keys, and merges
  *                         items cut between workgroups (a task-scheduled
  *                         decode, as the PrimTS kernels of TensorRT-LLM PR
- *                         #17399 are described in its "Description"); mixed
- *                         runs then use the heuristic split factor.  The
- *                         heuristic (0) itself picks balanced decode wherever
- *                         it would split.
+ *                         #17399 are described in its "Description"); and
+ *                         pa_run_mixed runs the task-queue schedule: one
+ *                         persistent workgroup per resident slot, drawing
+ *                         (q-block, KV head) items from a prefill-type and a
+ *                         decode-type queue (each sequence's q-blocks
+ *                         most-keys-first) until both are empty, never
+ *                         splitting keys.  The heuristic (0) picks balanced
+ *                         decode wherever it would split, and the task queues
+ *                         for mixed runs wherever it would not.
  *   num_cus               compute units to plan for; 0 = query the current device
  *                         (>0 lets plans be built without a GPU)
  *   q_dtype               PA_Q_BF16, or PA_Q_FP8_E4M3: queries arrive as E4M3
@@ -208,6 +213,7 @@ typedef struct {
   int32_t mixed_q_block_tokens;  /* query tokens per work item of mixed runs */
   int32_t balanced_workgroups;   /* > 0: balanced decode with this many workgroups */
   size_t workspace_bytes;    /* = pa_workspace_bytes(plan) */
+  int32_t queue_workgroups;  /* > 0: mixed runs use the task queues with this many workgroups */
 } pa_plan_info;
 
 /* Validate a shape description and build a plan.  Host only; uses the HIP
@@ -239,7 +245,9 @@ pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream)
 /* Unified mixed batch: any mix of q_len_b in one main launch.  Short rows
  * (q_len_b * G <= 32) take the decode schedule, longer ones the prefill
  * schedule, both inside the same kernel; split-KV and the merge pass as for
- * decode. */
+ * decode.  A plan with num_splits = -1 runs the task-queue schedule instead
+ * (a one-workgroup setup launch that lays out the queues in the workspace,
+ * then the persistent main launch; no merge). */
 pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /*

@@ -106,6 +106,7 @@ class pa_plan_info(ctypes.Structure):
         ("mixed_q_block_tokens", ctypes.c_int32),
         ("balanced_workgroups", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("queue_workgroups", ctypes.c_int32),
     ]
 
 

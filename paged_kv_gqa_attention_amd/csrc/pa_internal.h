@@ -53,6 +53,24 @@ struct AttnParams {
   int32_t head_groups;          // MLA: groups of up to 64 query heads per item (group = heads per group)
   int32_t q_fp8;                // queries are E4M3 codes (streamed fp8 prefill only)
   const float* q_descale;       // device scalar, fp8 queries
+  int32_t queue;                // mixed only: persistent workgroups pull items from
+                                // the task queues in sched (queue_sched_ints ints)
+};
+
+// Task queues of a mixed launch, in the workspace (int32 words): two draw
+// counters (prefill-type and decode-type items), kQueueSlots arrival counters
+// (one per compute unit id), then the item offsets of each sequence in the
+// prefill-type list [B+1] and in the decode-type list [B+1].
+constexpr int kQueueSlots = 1024;
+inline int64_t queue_sched_ints(int64_t num_seqs) { return 2 + kQueueSlots + 2 * (num_seqs + 1); }
+
+struct QueueSetupParams {
+  const int32_t* cu_q_lens;     // [B+1]
+  int32_t* sched;               // queue_sched_ints(B) words
+  int32_t num_seqs;
+  int32_t group;                // G
+  int32_t num_kv_heads;
+  int32_t q_block_tokens;       // tokens per prefill-type item
 };
 
 struct MergeParams {
@@ -112,6 +130,7 @@ struct BalancedMergeParams {
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream);
 // Launch the merge of balanced decode pieces.
 hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream);
+hipError_t launch_queue_setup(const QueueSetupParams& p, hipStream_t stream);
 
 // Launch the KV-cache append.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);

@@ -1368,13 +1368,152 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
   }
 }
 
+// Task-queue schedule of a mixed batch.  Work items are split into two lists
+// by the kind of work: prefill-type items (sequence b with q_len_b * G > 32:
+// one per (q-block, KV head), each sequence's q-blocks last-first, i.e. most
+// keys first) are compute-bound, decode-type items (one per (sequence, KV
+// head)) are memory-bound.  queue_setup_kernel lays both lists out (per
+// sequence offsets) and zeroes the counters.  The grid holds the workgroups
+// that fit on the device at once; each one draws items from the two lists
+// with an atomic counter per list until both are empty.  The first workgroup
+// to arrive on a compute unit prefers the prefill list and the second the
+// decode list, so that a compute-bound and a memory-bound item tend to share
+// each compute unit; a workgroup whose preferred list is empty takes the
+// other.  Every draw either claims one of the finitely many items or finds
+// both lists empty, so every workgroup ends without waiting on another.
+constexpr int kQmPref = 8;      // LDS metadata words used by the queue loop
+constexpr int kQmWhich = 9;
+constexpr int kQmItem = 10;
+constexpr int kQmSeq = 11;
+
+template <int D, bool FP8, int MODE>
+__device__ void queue_mixed(const AttnParams& p, uint8_t* smem, int32_t* pcache, int* meta) {
+  constexpr int NTH = Block<MODE, D>::threads;
+  const int B = p.num_seqs;
+  if (threadIdx.x == 0) meta[kQmPref] = atomicAdd(&p.sched[2 + (__smid() & (kQueueSlots - 1))], 1) & 1;
+  __syncthreads();
+  int pref = meta[kQmPref];
+  for (;;) {
+    __syncthreads();                            // the previous item is done with LDS and meta
+    if (threadIdx.x == 0) {
+      // list l's offsets start at sched + 2 + kQueueSlots + l (B + 1); its
+      // item count is the last offset
+      const int32_t* lists = p.sched + 2 + kQueueSlots;
+      int which = pref;
+      int k = atomicAdd(&p.sched[which], 1);
+      if (k >= lists[which * (B + 1) + B]) {
+        which ^= 1;
+        k = atomicAdd(&p.sched[which], 1);
+        if (k >= lists[which * (B + 1) + B]) k = -1;
+      }
+      meta[kQmWhich] = which;
+      meta[kQmItem] = k;
+      meta[kQmSeq] = -1;
+    }
+    __syncthreads();
+    const int which = meta[kQmWhich];
+    const int k = meta[kQmItem];
+    if (k < 0) break;
+    pref = which;
+    // the sequence whose range [off[b], off[b+1]) holds item k
+    const int32_t* off = p.sched + 2 + kQueueSlots + which * (B + 1);
+    for (int j = threadIdx.x; j < B; j += NTH)
+      if (off[j] <= k && k < off[j + 1]) meta[kQmSeq] = j;
+    __syncthreads();
+    const int b = meta[kQmSeq];
+    if (b < 0) break;                           // counters not set up: nothing to claim
+    const int r = k - off[b];
+    const int t0 = p.cu_q_lens[b];
+    const int q_len = p.cu_q_lens[b + 1] - t0;
+    const int BQ = p.q_block_tokens;
+    int g, i0, ntok;
+    if (which == 0) {
+      const int nb = (q_len + BQ - 1) / BQ;
+      g = r % p.num_kv_heads;
+      i0 = (nb - 1 - r / p.num_kv_heads) * BQ;
+      ntok = min(BQ, q_len - i0);
+    } else {
+      g = r;
+      i0 = 0;
+      ntok = q_len;
+    }
+    RowMap rm;
+    PageWalk pw;
+    const int L = item_setup<D, FP8>(p, b, g, t0 + i0, ntok, q_len, i0, rm, pw);
+    float c, vdesc;
+    score_scales<FP8>(p, c, vdesc);
+    if (which == 0)
+      rowsplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, c, vdesc);
+    else
+      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, 0, L, -1, c, vdesc);
+  }
+}
+
+// Lays out the two item lists of the task-queue schedule (one workgroup):
+// per-sequence item counts, an exclusive scan over the batch, and zeroed
+// draw and arrival counters.
+__global__ __launch_bounds__(1024) void queue_setup_kernel(QueueSetupParams q) {
+  __shared__ int sp[1024];
+  __shared__ int sd[1024];
+  const int B = q.num_seqs;
+  const int t = threadIdx.x;
+  const int per = (B + 1023) / 1024;
+  const int j0 = min(B, t * per);
+  const int j1 = min(B, j0 + per);
+  auto counts = [&](int j, int& np, int& nd) {
+    const int ql = q.cu_q_lens[j + 1] - q.cu_q_lens[j];
+    np = nd = 0;
+    if (ql <= 0) return;
+    if (ql * q.group > kCols) np = (ql + q.q_block_tokens - 1) / q.q_block_tokens * q.num_kv_heads;
+    else nd = q.num_kv_heads;
+  };
+  int cp = 0, cd = 0;
+  for (int j = j0; j < j1; ++j) {
+    int np, nd;
+    counts(j, np, nd);
+    cp += np;
+    cd += nd;
+  }
+  sp[t] = cp;
+  sd[t] = cd;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {       // inclusive scan
+    const int a = t >= o ? sp[t - o] : 0;
+    const int d = t >= o ? sd[t - o] : 0;
+    __syncthreads();
+    sp[t] += a;
+    sd[t] += d;
+    __syncthreads();
+  }
+  int32_t* offp = q.sched + 2 + kQueueSlots;
+  int32_t* offd = offp + B + 1;
+  int ep = sp[t] - cp, ed = sd[t] - cd;
+  for (int j = j0; j < j1; ++j) {
+    int np, nd;
+    counts(j, np, nd);
+    offp[j] = ep;
+    offd[j] = ed;
+    ep += np;
+    ed += nd;
+  }
+  if (t == 1023) {
+    offp[B] = sp[1023];
+    offd[B] = sd[1023];
+  }
+  if (t < 2) q.sched[t] = 0;
+  for (int i = t; i < kQueueSlots; i += 1024) q.sched[2 + i] = 0;
+}
+
 // QF8: queries arrive as E4M3 codes (fp8 inputs); only the streamed prefill
-// of an fp8 cache has that variant.
-template <int D, bool FP8, int MODE, bool QF8 = false>
+// of an fp8 cache has that variant.  QUEUE: the task-queue schedule of a
+// mixed batch (its own instance, so that its loop does not change the
+// register allocation of the one-item-per-workgroup kernel).
+template <int D, bool FP8, int MODE, bool QF8 = false, bool QUEUE = false>
 __global__ __launch_bounds__((Block<MODE, D>::threads))
 __attribute__((amdgpu_waves_per_eu(Block<MODE, D>::waves_per_eu, Block<MODE, D>::waves_per_eu)))
 void attn_kernel(AttnParams p) {
   static_assert(!QF8 || (FP8 && MODE == kPrefill && Block<MODE, D>::stream), "fp8 queries: streamed fp8 prefill only");
+  static_assert(!QUEUE || MODE == kMixed, "task queues: mixed batches only");
   __shared__ __attribute__((aligned(16))) uint8_t smem[Lds<D, FP8, MODE>::bytes];
   int* meta = reinterpret_cast<int*>(smem + Lds<D, FP8, MODE>::base);
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + Lds<D, FP8, MODE>::pcache_off);
@@ -1383,6 +1522,10 @@ void attn_kernel(AttnParams p) {
       balanced_decode<D, FP8, MODE>(p, smem, pcache, meta);
       return;
     }
+  }
+  if constexpr (QUEUE) {
+    queue_mixed<D, FP8, MODE>(p, smem, pcache, meta);
+    return;
   }
   const int split = blockIdx.z;
   int g = blockIdx.y;
@@ -2092,6 +2235,13 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
     }
   }
   if (p.q_fp8) return hipErrorInvalidValue;
+  if constexpr (MODE == kMixed) {
+    if (p.queue) {
+      hipLaunchKernelGGL((attn_kernel<D, FP8, MODE, false, true>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.queue) return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
   return hipGetLastError();
 }
@@ -2212,6 +2362,12 @@ hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hip
     case 512: hipLaunchKernelGGL(merge_balanced_kernel<512>, grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_queue_setup(const QueueSetupParams& p, hipStream_t stream) {
+  if (p.num_seqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(queue_setup_kernel, dim3(1), dim3(1024), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -107,10 +107,12 @@ def test_split_heuristic_and_workspace():
     assert W == 256
     assert B.pa_workspace_bytes(p) >= 2 * W * 32 * (256 + 1) * 4 + (4 + 64 + 1) * 4
     B.pa_plan_destroy(p)
-    # many items: no split, no balanced decode, no workspace
+    # many items: no split, no balanced decode; mixed runs on the task queues,
+    # whose workspace is all the plan needs
     p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048))
     info = B.pa_plan_get_info(p)
-    assert info.num_splits == 1 and info.balanced_workgroups == 0 and B.pa_workspace_bytes(p) == 0
+    assert info.num_splits == 1 and info.balanced_workgroups == 0 and info.queue_workgroups == 512
+    assert B.pa_workspace_bytes(p) == ((2 + 1024 + 2 * 257) * 4 + 255) // 256 * 256
     B.pa_plan_destroy(p)
     # balanced decode on request; below -1 is invalid
     p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048,
@@ -120,6 +122,18 @@ def test_split_heuristic_and_workspace():
     assert B.pa_workspace_bytes(p) >= 2 * 512 * 4 * (128 + 1) * 4
     B.pa_plan_destroy(p)
     assert plan_status(num_splits=-2) == B.PA_ERR_INVALID
+    # -1 also puts mixed runs on the task queues: one workgroup per resident
+    # slot of the mixed kernel (two per CU at D 128 bf16); the workspace holds
+    # 2 counters, 1024 arrival counters and two offset lists of B + 1
+    assert info.queue_workgroups == 2 * 256
+    assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 257) * 4
+    p = B.pa_plan(desc(num_seqs=4096, page_table_cols=16, max_total_q=4096, num_splits=-1))
+    assert B.pa_plan_get_info(p).queue_workgroups == 512
+    assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 4097) * 4
+    B.pa_plan_destroy(p)
+    p = B.pa_plan(desc(num_splits=1))
+    assert B.pa_plan_get_info(p).queue_workgroups == 0
+    B.pa_plan_destroy(p)
     # forced splits are honoured (rounded to whole 128-key windows)
     p = B.pa_plan(desc(num_splits=3, page_table_cols=64, max_seq_len=1024))
     info = B.pa_plan_get_info(p)
@@ -176,6 +190,10 @@ def test_runs_reject_bad_arguments_without_touching_the_device():
     x.q_descale = 32776
     x.q_stride_t = 32 * 128 + 8
     assert B.lib().pa_run_prefill(p, ctypes.byref(x), None) == B.PA_ERR_INVALID   # row not 16-byte
+    B.pa_plan_destroy(p)
+    # a task-queue plan: mixed runs need the workspace
+    p = B.pa_plan(desc(num_splits=-1))
+    assert B.lib().pa_run_mixed(p, ctypes.byref(args()), None) == B.PA_ERR_WORKSPACE
     B.pa_plan_destroy(p)
     # a split plan without workspace
     p = B.pa_plan(desc(num_splits=4, page_table_cols=64, max_seq_len=1024))

@@ -1,0 +1,97 @@
+"""Host model of the task-queue schedule of mixed batches (the setup
+kernel's per-sequence item lists and the main kernel's item -> (sequence,
+q-block, KV head) mapping), checked over random batches: every q-block of
+every KV head is claimed exactly once, the prefill-type list holds exactly
+the sequences with q_len * G > 32, and each sequence's q-blocks come
+most-keys-first.  Mirrors queue_setup_kernel and queue_mixed; no GPU."""
+import numpy as np
+import pytest
+
+KCOLS = 32
+THREADS = 1024
+
+
+def setup_lists(q_lens, G, Hkv, BQ):
+    B = len(q_lens)
+    per = (B + THREADS - 1) // THREADS
+    npf = np.zeros(B, np.int64)
+    ndc = np.zeros(B, np.int64)
+    for j, ql in enumerate(q_lens):
+        if ql <= 0:
+            continue
+        if ql * G > KCOLS:
+            npf[j] = (ql + BQ - 1) // BQ * Hkv
+        else:
+            ndc[j] = Hkv
+    # the kernel: per-thread chunk sums, an inclusive scan over 1024 threads,
+    # then a sequential exclusive scan inside each chunk
+    cp = np.array([npf[min(B, t * per):min(B, t * per + per)].sum() for t in range(THREADS)])
+    cd = np.array([ndc[min(B, t * per):min(B, t * per + per)].sum() for t in range(THREADS)])
+    sp, sd = np.cumsum(cp), np.cumsum(cd)
+    offp = np.zeros(B + 1, np.int64)
+    offd = np.zeros(B + 1, np.int64)
+    for t in range(THREADS):
+        ep, ed = sp[t] - cp[t], sd[t] - cd[t]
+        for j in range(min(B, t * per), min(B, t * per + per)):
+            offp[j], offd[j] = ep, ed
+            ep += npf[j]
+            ed += ndc[j]
+    offp[B], offd[B] = sp[-1], sd[-1]
+    return offp, offd
+
+
+def claim(which, ks, off, q_lens, Hkv, BQ):
+    """Items ks of one list -> (b, g, i0, ntok) arrays: b is the one sequence
+    whose range [off[b], off[b+1]) holds k (the kernel finds it by testing
+    every range)."""
+    b = np.searchsorted(off, ks, side="right") - 1
+    assert np.all((off[b] <= ks) & (ks < off[b + 1]))
+    r = ks - off[b]
+    ql = q_lens[b]
+    if which == 0:
+        nb = (ql + BQ - 1) // BQ
+        g = r % Hkv
+        i0 = (nb - 1 - r // Hkv) * BQ
+        ntok = np.minimum(BQ, ql - i0)
+    else:
+        g, i0, ntok = r, np.zeros_like(r), ql
+    return b, g, i0, ntok
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_queue_lists_cover_every_item_once(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.choice([1, 3, 17, 300, 1500, 2500]))
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    Hkv = int(rng.choice([1, 2, 8]))
+    BQ = max(1, 128 // G)
+    kind = rng.random(B)
+    q_lens = np.where(kind < 0.15, 0, np.where(kind < 0.6, rng.integers(1, 3, B),
+                                                rng.integers(1, 700, B))).astype(np.int64)
+    offp, offd = setup_lists(q_lens, G, Hkv, BQ)
+    seen = {}
+    last_i0 = {}
+    for which, off in ((0, offp), (1, offd)):
+        ks = np.arange(int(off[-1]), dtype=np.int64)
+        bs, gs, i0s, ntoks = claim(which, ks, off, q_lens, Hkv, BQ)
+        assert np.all((gs >= 0) & (gs < Hkv) & (i0s >= 0) & (ntoks >= 1) & (i0s + ntoks <= q_lens[bs]))
+        for b, g, i0 in zip(bs.tolist(), gs.tolist(), i0s.tolist()):
+            key = (b, i0, g)
+            assert key not in seen
+            seen[key] = which
+            # q-blocks of one (sequence, head): most keys first
+            if (b, g) in last_i0:
+                assert i0 < last_i0[(b, g)]
+            last_i0[(b, g)] = i0
+    want = {}
+    for b, ql in enumerate(q_lens):
+        if ql <= 0:
+            continue
+        if ql * G > KCOLS:
+            for qb in range((ql + BQ - 1) // BQ):
+                for g in range(Hkv):
+                    want[(b, qb * BQ, g)] = 0
+        else:
+            for g in range(Hkv):
+                want[(b, 0, g)] = 1
+    assert seen == want
