@@ -1944,7 +1944,8 @@ __device__ void mla_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, in
 // softmax is split four ways (mla_keys), and wave w accumulates the value
 // columns [128 w, 128 w + 128).  No product is computed twice.  More than 64
 // heads take several head groups (their score and accumulator registers
-// would not fit one wave).
+// would not fit one wave).  Used for groups of up to 32 heads (NCT = 1);
+// larger groups run mla_hs_kernel.
 //   Split schedule: one workgroup per (b, window, group); items are ordered
 //   (b, split, group) and dealt so that each XCD takes a contiguous run of
 //   them, which puts the head groups of one window on one L2.
@@ -2006,6 +2007,305 @@ void mla_kernel(AttnParams p) {
   // the last window takes every remaining key
   const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
   mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
+}
+
+// LDS of a head-split MLA workgroup: a ring of 32-key tiles, then the
+// page-id cache.
+struct MlaHsLds {
+  static constexpr int ring = 4;
+  static constexpr int pcache_off = ring * MlaGeo::tile_bytes + 64;
+  static constexpr int bytes = pcache_off + kPcacheEntries * 4;
+  static_assert(bytes <= kLdsMax, "MLA LDS budget exceeded");
+};
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+constexpr int kMlaHeads = 16;                    // query heads per wave
+constexpr int kMlaQSteps = kMlaDk / 32;          // 32-wide k-steps of the score product
+constexpr int kMlaVTiles = kMlaLatent / 16;      // 16-wide value tiles of O
+
+// Running state of one wave: its 16 heads over its keys.  Lane l holds head
+// l % 16; o[t][i] is output column 16 t + 4 (l / 16) + i; l is this lane's
+// part of the row sum (its four keys of each block); m is the same on the
+// four lanes of a head.
+struct MlaState {
+  f32x4 o[kMlaVTiles];
+  float m, l;
+};
+
+// One 16-key block (rows kr .. kr + 15 of the LDS tile at kl; keys key0 ..
+// key0 + 15, of which those >= khi are masked): scores S^T = K Q^T on
+// 16x16x32 MFMAs (lane l: head l % 16, keys 4 (l / 16) .. +3), the online
+// softmax, and O^T += V^T P^T on 16x16x16 MFMAs, P straight from the score
+// registers (the B operand layout of the 16x16x16 product is the accumulator
+// layout of the score product).  V^T operands come from transposing LDS
+// reads: 16-lane group g reads keys 4 g .. 4 g + 3 of 16 columns and lane L
+// receives column L's four keys.
+template <bool CAP>
+__device__ __forceinline__ void mla_block(MlaState& st, const uint8_t* kl, int kr, int key0, int khi,
+                                          const bf16x8 (&qreg)[kMlaQSteps], float c, const SoftCap& sc,
+                                          int lane) {
+  // One wave per SIMD: every LDS operand read is issued one step ahead of
+  // the MFMAs that consume it (scheduling barriers keep that order), so its
+  // latency hides behind the previous step's products.
+  constexpr int NP = kMlaQSteps / 2;            // pairs of score k-steps
+  constexpr int VG = 4;                         // value tiles per step
+  const uint8_t* krow = kl + (kr + (lane & 15)) * MlaGeo::pitch + 16 * (lane >> 4);
+  const int L = lane & 15;
+  const uint8_t* vsrc = kl + (kr + 4 * (lane >> 4) + (L >> 2)) * MlaGeo::pitch + 8 * (L & 3);
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  u32x4 ka[NP][2];
+  ka[0][0] = *reinterpret_cast<const u32x4*>(krow);
+  ka[0][1] = *reinterpret_cast<const u32x4*>(krow + 64);
+#pragma unroll
+  for (int jp = 0; jp < NP; ++jp) {
+    if (jp + 1 < NP) {
+      ka[jp + 1][0] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1));
+      ka[jp + 1][1] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1) + 64);
+    }
+    s0 = mfma16_k32(as_bf16x8(ka[jp][0]), qreg[2 * jp], s0);
+    s1 = mfma16_k32(as_bf16x8(ka[jp][1]), qreg[2 * jp + 1], s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the first value operands load while the softmax runs
+  i16x4 va[kMlaVTiles / VG][VG];
+#pragma unroll
+  for (int u = 0; u < VG; ++u) va[0][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * u));
+  __builtin_amdgcn_sched_barrier(0);
+  const int kb = key0 + 4 * (lane >> 4);
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x = s0[i] + s1[i];
+    if constexpr (CAP) x = cap1(x, sc);
+    v[i] = kb + i < khi ? x : neg_inf();
+  }
+  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, xor32(mx));
+  const float mxs = mx * c;
+  if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
+    // rare (the running maximum grew by more than the slack): kept a branch,
+    // so that the accumulator is touched only here
+    __asm__ volatile("" ::: "memory");
+    const float m_new = fmaxf(st.m, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < kMlaVTiles; ++t) st.o[t] *= alpha;
+    st.m = m_new;
+  }
+  const float nref = st.m == neg_inf() ? 0.f : -st.m;
+  float pr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], c, nref));
+  st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  const u32x2 pw{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+  const bf16x4 pb = __builtin_bit_cast(bf16x4, pw);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < kMlaVTiles / VG; ++g) {
+    if (g + 1 < kMlaVTiles / VG) {
+#pragma unroll
+      for (int u = 0; u < VG; ++u)
+        va[g + 1][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * (VG * (g + 1) + u)));
+    }
+#pragma unroll
+    for (int u = 0; u < VG; ++u)
+      st.o[VG * g + u] = mfma16_k16(__builtin_bit_cast(bf16x4, va[g][u]), pb, st.o[VG * g + u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The key loop of a head-split MLA item: 32-key tiles of latent rows stream
+// through a ring of four LDS buffers by direct loads (issued three tiles
+// ahead, so that about 110 KB per compute unit are in flight; one barrier per
+// tile); every wave runs both 16-key blocks of each tile for its heads.
+template <bool CAP>
+__device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
+                                         int klo, int khi, const bf16x8 (&qreg)[kMlaQSteps], float c,
+                                         const SoftCap& sc, MlaState& st, int wave, int lane) {
+  constexpr int R = MlaHsLds::ring;
+  PageWalk w;
+  w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
+  w.page_bytes = p.kv_page_bytes;
+  w.head_off = 0;
+  w.row_stride_b = MlaGeo::row_bytes;
+  w.shift = p.page_shift;
+  w.klimit = L;
+  MlaLoads ml;
+  ml.init(wave, lane);
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    wait_vmem_all();                            // Q loads and page-table reads
+    __syncthreads();
+    const int ntiles = (ce - cb + kSub - 1) / kSub;
+#pragma unroll
+    for (int t = 0; t < R - 1; ++t)
+      if (t < ntiles) ml.issue(p.k_pool, w, cb + t * kSub, smem + t * MlaGeo::tile_bytes, wave);
+    static_assert(R == 4, "the waits below count two tiles in flight");
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t must have landed; the (up to R-2) later tiles already issued
+      // may stay in flight (loads retire in order; each tile is at least
+      // min_per_wave loads of this wave)
+      const int ahead = min(R - 2, ntiles - 1 - t);
+      if (ahead >= 2)
+        wait_vmem<2 * MlaGeo::min_per_wave>();
+      else if (ahead == 1)
+        wait_vmem<MlaGeo::min_per_wave>();
+      else
+        wait_vmem<0>();
+      ring_barrier();
+      // the loads of tile t + R - 1 go into the buffer read in the previous
+      // iteration, which every wave has left (barrier above)
+      if (t + R - 1 < ntiles)
+        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
+      const uint8_t* kl = smem + (t % R) * MlaGeo::tile_bytes;
+      const int k0 = cb + t * kSub;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int key0 = k0 + 16 * hb;
+        if (key0 < ce) mla_block<CAP>(st, kl, 16 * hb, key0, khi, qreg, c, sc, lane);
+      }
+    }
+  }
+}
+
+// One head-split MLA item: the keys [klo, khi) of sequence b for head group
+// hg (p.group heads starting at hg * p.group; wave w takes heads
+// 16 w .. 16 w + 15 of it), then its outputs -- final rows (slot < 0), a
+// split-KV partial record (split schedule) or a balanced partial record in
+// slot `slot`.
+__device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int hg, int L, int klo,
+                            int khi, int slot, int wave, int lane) {
+  const int hl = wave * kMlaHeads + (lane & 15);  // head within the group
+  const int h = hg * p.group + hl;
+  const bool hok = hl < p.group && h < p.num_q_heads;
+  // the B operand of k-step j: head hl's query values 32 j + 8 (lane / 16) .. +7
+  bf16x8 qreg[kMlaQSteps];
+  {
+    const uint16_t* src = p.q + (int64_t)b * p.q_stride_t + (int64_t)(hok ? h : 0) * kMlaDk + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < kMlaQSteps; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 32 * j);
+      qreg[j] = as_bf16x8(hok ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  float c, vdesc;
+  score_scales<false>(p, c, vdesc);
+  const SoftCap sc(p.softcap, c);
+  MlaState st;
+#pragma unroll
+  for (int t = 0; t < kMlaVTiles; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = neg_inf();
+  st.l = 0.f;
+  if (khi > klo) {
+    if (sc.on())
+      mla_hs_keys<true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
+    else
+      mla_hs_keys<false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
+  }
+  // the row sum: this lane's keys, then the head's four lanes
+  st.l += __shfl_xor(st.l, 16);
+  st.l += xor32(st.l);
+  if (!hok) return;
+  const bool empty = !(st.l > 0.f);
+  const float inv = empty ? 0.f : vdesc / st.l;
+  const float lse2 = empty ? neg_inf() : st.m + __builtin_amdgcn_logf(st.l);
+  const int d_lane = 4 * (lane >> 4);
+  if (slot >= 0) {
+    // balanced records hold the group's rows (p.group of them) per slot
+    const int64_t row = p.balanced ? (int64_t)slot * p.group + hl
+                                   : ((int64_t)slot * p.max_total_q + b) * p.num_q_heads + h;
+    if (lane < 16) p.part_lse[row] = lse2;
+    if (empty) return;
+    float* dst = p.part_o + row * kMlaLatent + d_lane;
+#pragma unroll
+    for (int t = 0; t < kMlaVTiles; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = st.o[t] * inv;
+  } else {
+    uint16_t* dst = p.out + (int64_t)b * p.o_stride_t + (int64_t)h * kMlaLatent + d_lane;
+#pragma unroll
+    for (int t = 0; t < kMlaVTiles; ++t)
+      *reinterpret_cast<u32x2*>(dst + 16 * t) =
+          u32x2{pack_bf16x2(st.o[t][0] * inv, st.o[t][1] * inv), pack_bf16x2(st.o[t][2] * inv, st.o[t][3] * inv)};
+    if (p.lse && lane < 16) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
+  }
+}
+
+// Head-split MLA decode, for head groups of 33 to 64 heads.  Item =
+// (sequence b, key window, head group).  Each wave owns 16 query heads of the
+// group (their 576 query values in registers, 72 VGPRs) and computes complete
+// scores for them over every key (16x16x32 MFMAs), its own online softmax,
+// and all 512 value columns of its heads (16x16x16 MFMAs, P straight from the
+// score registers), so the key loop has no exchange between waves besides the
+// tile barrier.  Each wave reads the whole tile from LDS (K for the scores,
+// its first 512 columns transposed as the value operand); the cache is read
+// from memory once per head group.  Schedules (split, balanced) as in
+// mla_kernel.
+__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_hs_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MlaHsLds::bytes];
+  int32_t* pcache = reinterpret_cast<int32_t*>(smem + MlaHsLds::pcache_off);
+  int* meta = reinterpret_cast<int*>(smem + MlaHsLds::pcache_off - 64);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (p.balanced) {
+    const int HG = p.head_groups;
+    const int w = blockIdx.x;
+    int u0, u1, b, S;
+    if (!balanced_start<kDecWaves * kWave>(p, smem, meta, HG, u0, u1, b, S)) return;
+    int u = u0;
+    int piece = 0;
+    while (u < u1) {
+      const int sb = seq_units(p, b);
+      const int item0 = HG * S;
+      if (sb == 0 || u >= item0 + HG * sb) {    // past this sequence's items
+        S += sb;
+        ++b;
+        continue;
+      }
+      const int hg = (u - item0) / sb;
+      const int a0 = item0 + hg * sb;
+      const int a1 = a0 + sb;
+      const int pu1 = min(u1, a1);
+      const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+      const int klo = (u - a0) << kUnitShift;
+      const int khi = min(L, (pu1 - a0) << kUnitShift);
+      const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
+      mla_hs_item(p, smem, pcache, b, hg, L, klo, khi, slot, wave, lane);
+      __syncthreads();                          // LDS is reused by the next piece
+      u = pu1;
+      ++piece;
+    }
+    return;
+  }
+  int hg, b, split;
+  {
+    const int n = gridDim.x;
+    const int lin = blockIdx.x;
+    const int full = n - n % kXcds;
+    const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
+    hg = logical % p.head_groups;
+    const int rest = logical / p.head_groups;
+    split = rest % p.num_splits;
+    b = rest / p.num_splits;
+  }
+  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
+  const int klo = split * p.split_keys;
+  // the last window takes every remaining key
+  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
+  mla_hs_item(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -2345,9 +2645,11 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
   const dim3 block(kDecWaves * kWave);
-  if (p.num_q_heads <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, block, 0, stream, p);
-  else if (p.num_q_heads <= 128) hipLaunchKernelGGL(mla_kernel<2>, grid, block, 0, stream, p);
-  else return hipErrorInvalidValue;
+  // groups of up to 32 heads: column split (the waves share each score);
+  // 33 to 64: head split (16 heads per wave)
+  if (p.num_q_heads > 128 || p.group > 64 || p.group < 1) return hipErrorInvalidValue;
+  if (p.group <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(mla_hs_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
