@@ -292,6 +292,34 @@ typedef struct {
 
 pa_status pa_run_append(pa_plan_t plan, const pa_append_args* args, hipStream_t stream);
 
+/*
+ * Device-content check of a run's metadata (a debugging aid).  The runs
+ * trust what the device arrays hold: a page id outside the pool, a query run
+ * longer than its sequence or a sequence longer than its page-table row is
+ * undefined behaviour there, as the planning contract of TensorRT-LLM PR
+ * #17399 leaves it ("Unified page-table metadata": the page table and live
+ * lengths are the caller's).  This call scans the metadata of `args` on
+ * `stream` and writes a mask of what it finds into the device int32 *flags
+ * (0 = clean); it reads only the metadata (never a page id as an address),
+ * allocates nothing and is graph-capturable.  Bits:
+ *   PA_CHECK_PAGE_ID    a page-table column that holds live keys names a page
+ *                       outside [0, num_pages)
+ *   PA_CHECK_Q_LEN      q_len_b > seq_lens[b] > 0 (queries are the last keys)
+ *   PA_CHECK_SEQ_LEN    seq_lens[b] < 0 or > page_table_cols * page_size
+ *   PA_CHECK_CU_Q_LENS  cu_q_lens decreasing, not starting at 0, or its total
+ *                       above the plan's max_total_q
+ * Uses page_table, cu_q_lens (NULL: one token per sequence), seq_lens.
+ * Returns PA_ERR_INVALID for NULL plan, args or flags, or NULL metadata when
+ * num_seqs > 0.
+ */
+enum {
+  PA_CHECK_PAGE_ID = 1,
+  PA_CHECK_Q_LEN = 2,
+  PA_CHECK_SEQ_LEN = 4,
+  PA_CHECK_CU_Q_LENS = 8
+};
+pa_status pa_check_metadata(pa_plan_t plan, const pa_args* args, int32_t* flags, hipStream_t stream);
+
 /* Release a plan (NULL is ignored). */
 void pa_plan_destroy(pa_plan_t plan);
 

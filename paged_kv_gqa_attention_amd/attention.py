@@ -80,6 +80,13 @@ class PagedAttention:
                            softcap=self.w.softcap if softcap is None else softcap,
                            q_descale=x.q_descale)
 
+    def check(self, x: DeviceInputs) -> int:
+        """Mask of metadata violations found on the device (0 = clean)."""
+        flags = torch.full((1,), -1, dtype=torch.int32, device=self.device)
+        a = self.args(x, None, None)                  # the check reads metadata only
+        B.pa_check_metadata(self.plan, a, flags, B.current_stream())
+        return int(flags.item())
+
     def new_outputs(self, x: DeviceInputs):
         T, Hq, D = x.q.shape                 # bf16 values or E4M3 codes: the same shape
         out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=self.device)

@@ -39,7 +39,12 @@ PA_Q_FP8_E4M3 = 1
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
            "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str",
            "pa_mla_plan", "pa_mla_workspace_bytes", "pa_mla_num_splits", "pa_run_mla_decode",
-           "pa_mla_plan_destroy")
+           "pa_mla_plan_destroy", "pa_check_metadata")
+
+PA_CHECK_PAGE_ID = 1
+PA_CHECK_Q_LEN = 2
+PA_CHECK_SEQ_LEN = 4
+PA_CHECK_CU_Q_LENS = 8
 
 
 class PaLibraryMissing(RuntimeError):
@@ -184,6 +189,8 @@ def lib():
         L.pa_run_append.restype = ctypes.c_int
         L.pa_plan_destroy.argtypes = [vp]
         L.pa_plan_destroy.restype = None
+        L.pa_check_metadata.argtypes = [vp, ctypes.POINTER(pa_args), vp, vp]
+        L.pa_check_metadata.restype = ctypes.c_int
         L.pa_status_str.argtypes = [ctypes.c_int]
         L.pa_status_str.restype = ctypes.c_char_p
         L.pa_mla_plan.argtypes = [ctypes.POINTER(pa_mla_desc), ctypes.POINTER(vp)]
@@ -244,6 +251,14 @@ def pa_run_decode(plan, args: pa_args, stream) -> None:
 
 def pa_run_mixed(plan, args: pa_args, stream) -> None:
     _run("pa_run_mixed", plan, args, stream)
+
+
+def pa_check_metadata(plan, args: pa_args, flags, stream) -> None:
+    """Queue the metadata check; `flags` is a device int32 (tensor or pointer)."""
+    fp = _ptr(flags) if hasattr(flags, "data_ptr") else flags
+    rc = lib().pa_check_metadata(plan, ctypes.byref(args), ctypes.c_void_p(fp), ctypes.c_void_p(stream))
+    if rc != PA_OK:
+        raise PaError(rc, "pa_check_metadata")
 
 
 def pa_run_append(plan, args: "pa_append_args", stream) -> None:

@@ -190,6 +190,24 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info) {
   return PA_OK;
 }
 
+pa_status pa_check_metadata(pa_plan_t plan, const pa_args* a, int32_t* flags, hipStream_t stream) {
+  if (!plan || !a || !flags) return PA_ERR_INVALID;
+  const pa_desc& d = plan->d;
+  if (d.num_seqs > 0 && (!a->page_table || !a->seq_lens)) return PA_ERR_INVALID;
+  pa::CheckParams q;
+  q.page_table = a->page_table;
+  q.pt_row_stride = d.page_table_row_stride;
+  q.pt_cols = d.page_table_cols;
+  q.page_shift = plan->page_shift;
+  q.num_pages = d.num_pages;
+  q.cu_q_lens = a->cu_q_lens;
+  q.seq_lens = a->seq_lens;
+  q.num_seqs = d.num_seqs;
+  q.max_total_q = plan->rows_cap;
+  q.flags = flags;
+  return pa::launch_check(q, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_run_append(pa_plan_t plan, const pa_append_args* a, hipStream_t stream) {
   if (!plan || !a) return PA_ERR_INVALID;
   const pa_desc& d = plan->d;

@@ -132,6 +132,20 @@ hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream);
 hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hipStream_t stream);
 hipError_t launch_queue_setup(const QueueSetupParams& p, hipStream_t stream);
 
+struct CheckParams {
+  const int32_t* page_table;    // [B, pt_row_stride]
+  int32_t pt_row_stride;
+  int32_t pt_cols;
+  int32_t page_shift;
+  int32_t num_pages;
+  const int32_t* cu_q_lens;     // [B+1] or NULL (one token per sequence)
+  const int32_t* seq_lens;      // [B]
+  int32_t num_seqs;
+  int32_t max_total_q;
+  int32_t* flags;               // device int32 mask
+};
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
+
 // Launch the KV-cache append.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 

@@ -2667,6 +2667,44 @@ hipError_t launch_merge_balanced(int head_dim, const BalancedMergeParams& p, hip
   return hipGetLastError();
 }
 
+// Metadata check (pa_check_metadata): one thread per sequence; page ids
+// are read as values only.  The mask is cleared by a one-thread launch
+// before the check launch ORs into it.
+__global__ void check_clear_kernel(int32_t* flags) { *flags = 0; }
+
+__global__ __launch_bounds__(256) void check_kernel(CheckParams q) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= q.num_seqs) return;
+  int bits = 0;
+  const int L = q.seq_lens[b];
+  const int64_t cap = (int64_t)q.pt_cols << q.page_shift;
+  if (L < 0 || L > cap) bits |= 4;
+  int qn = 1;
+  if (q.cu_q_lens) {
+    const int c0 = q.cu_q_lens[b], c1 = q.cu_q_lens[b + 1];
+    qn = c1 - c0;
+    if (qn < 0 || (b == 0 && c0 != 0) || (b == q.num_seqs - 1 && c1 > q.max_total_q)) bits |= 8;
+  }
+  if (L > 0 && qn > L) bits |= 2;
+  const int64_t live = L > 0 ? min((int64_t)L, cap) : 0;
+  const int np = (int)((live + (1 << q.page_shift) - 1) >> q.page_shift);
+  const int32_t* row = q.page_table + (int64_t)b * q.pt_row_stride;
+  for (int c = 0; c < np; ++c) {
+    const int id = row[c];
+    if (id < 0 || id >= q.num_pages) {
+      bits |= 1;
+      break;
+    }
+  }
+  if (bits) atomicOr(q.flags, bits);
+}
+
+hipError_t launch_check(const CheckParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(check_clear_kernel, dim3(1), dim3(1), 0, stream, p.flags);
+  if (p.num_seqs > 0) hipLaunchKernelGGL(check_kernel, dim3((unsigned)((p.num_seqs + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_queue_setup(const QueueSetupParams& p, hipStream_t stream) {
   if (p.num_seqs <= 0) return hipSuccess;
   hipLaunchKernelGGL(queue_setup_kernel, dim3(1), dim3(1024), 0, stream, p);

@@ -278,3 +278,14 @@ def test_mla_plan():
         setattr(x, field, val)
         assert B.lib().pa_run_mla_decode(p, ctypes.byref(x), None) == B.PA_ERR_INVALID
     B.pa_mla_plan_destroy(p)
+
+
+def test_check_metadata_rejects_bad_arguments_without_touching_the_device():
+    p = B.pa_plan(desc())
+    a = B.pa_args()                       # page table and lengths NULL
+    assert B.lib().pa_check_metadata(p, ctypes.byref(a), ctypes.c_void_p(4096), None) == B.PA_ERR_INVALID
+    a.page_table, a.seq_lens = 8192, 12288
+    assert B.lib().pa_check_metadata(p, ctypes.byref(a), None, None) == B.PA_ERR_INVALID
+    assert B.lib().pa_check_metadata(None, ctypes.byref(a), ctypes.c_void_p(4096), None) == B.PA_ERR_INVALID
+    assert B.lib().pa_check_metadata(p, None, ctypes.c_void_p(4096), None) == B.PA_ERR_INVALID
+    B.pa_plan_destroy(p)
