@@ -292,9 +292,21 @@ def cpu_baseline(w, budget_s=10.0):
         nseq += take
         b = (b + take) % w.num_seqs
     return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d sequence passes over the %d-sequence batch (all %d query heads), "
                       "%.1f s of fp64 CPU work" % (nseq, w.num_seqs, Hq, elapsed)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
