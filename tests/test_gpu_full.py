@@ -65,3 +65,23 @@ def test_full_size_outputs_are_finite_everywhere():
         torch.cuda.synchronize()
         assert bool(torch.isfinite(out.float()).all()), w.name
         assert bool(torch.isfinite(lse).all()), w.name
+
+
+def test_large_batches_span_wide_grids():
+    # 6,000 short decode rows (a grid of 6,000 x 8 workgroups; plain,
+    # balanced and mixed) and a mixed batch of about 36,000 tokens (12 long
+    # prefills, 12 decode rows; over 1,000 q-blocks per KV head), checked on
+    # sampled rows
+    rng = np.random.default_rng(77)
+    L = rng.integers(1, 200, size=6000)
+    w = synth.build(name="decode_6000", seq_lens=L, q_lens=np.ones(6000, dtype=np.int64),
+                    num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16, seed=78)
+    run_sampled(w, "decode", per_seq=1, heads=2)
+    run_sampled(w, "decode", num_splits=-1, per_seq=1, heads=2)
+    run_sampled(w, "mixed", per_seq=1, heads=2)
+    L = rng.integers(2000, 4000, size=24)
+    q = np.where(np.arange(24) % 2 == 0, L, 1)
+    w = synth.build(name="mixed_36k", seq_lens=L, q_lens=q, num_q_heads=16, num_kv_heads=4,
+                    head_dim=64, page_size=32, seed=79)
+    run_sampled(w, "mixed", per_seq=3, heads=2)
+    run_sampled(w, "prefill", per_seq=3, heads=2)
