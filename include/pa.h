@@ -53,7 +53,8 @@
  *               (q_len_b > seq_lens[b], seq_lens[b] > C * page, a live page id
  *               outside [0, num_pages), cu_q_lens[B] > max_total_q) are the
  *               caller's responsibility; lengths are clamped so the kernels
- *               stay inside the buffers, page ids are not checked.
+ *               stay inside the buffers, page ids are not checked by the runs
+ *               (pa_check_metadata checks all of these on the device).
  *   Layouts     All element strides are in elements, not bytes.
  */
 #ifndef PA_H
