@@ -1,0 +1,47 @@
+"""bench.py host logic, without a GPU: one GPU only, the roofline constants,
+and the traffic figure read from a profile summary only while that summary
+was taken on the current kernel source."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_peaks():
+    assert abs(bench.BF16_PEAK_TFLOPS - 256 * 2.4e9 * 4096 / 1e12) < 0.1
+    assert bench.FP8_PEAK_TFLOPS == 2 * bench.BF16_PEAK_TFLOPS
+    # half the flops at each rate
+    t = 0.5 / bench.FP8_PEAK_TFLOPS + 0.5 / bench.BF16_PEAK_TFLOPS
+    assert abs(bench.FP8Q_PEAK_TFLOPS - 1.0 / t) < 1e-9
+    assert bench.HBM_PEAK_GBS == 8000.0
+
+
+def test_traffic_needs_the_current_kernel_hash(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.read_traffic("w") is None
+    p = tmp_path / "w_counters.md"
+    p.write_text("kernel_sha: %s\nhbm_bytes_per_launch: 1.5e+09\n" % bench.kernel_sha())
+    assert bench.read_traffic("w") == 1.5e9
+    p.write_text("kernel_sha: 0000000000000000\nhbm_bytes_per_launch: 1.5e+09\n")
+    assert bench.read_traffic("w") is None
+
+
+def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int f() { return 1; }  // one\n")
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    h = bench.kernel_sha()
+    src.write_text("/* a comment */\nint f() {\n  return 1;  // two\n}\n")
+    assert bench.kernel_sha() == h
+    src.write_text("int f() { return 2; }\n")
+    assert bench.kernel_sha() != h
