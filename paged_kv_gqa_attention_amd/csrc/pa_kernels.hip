@@ -84,6 +84,12 @@ struct Block {
   static constexpr int nct = 1;
   static constexpr int waves_per_eu = D == 256 ? 1 : (stream ? waves / 4 : 2);
 };
+
+// Decode of an fp8 cache at head dim 256 runs the ring schedule (ring_item):
+// each of the four waves streams its own 32-key steps through a private LDS
+// ring filled by direct global->LDS loads.
+template <int D, bool FP8, int MODE>
+struct RingDec { static constexpr bool value = MODE == kDecode && D == 256 && FP8; };
 constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
 constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
 constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
@@ -138,10 +144,34 @@ struct Geo {
   static constexpr int red_bytes = red_floats * kWave * 4;
 };
 
+// Byte geometry of the ring decode.  A half-step is the K rows (or the V rows)
+// of 32 keys, unpadded; bank conflicts are avoided by storing 16-byte chunk c
+// of row r at chunk position c ^ (r mod 16).  Each wave owns four half-step
+// buffers (K and V of two steps), filled by direct global->LDS loads of 1 KB.
+template <int D, bool FP8>
+struct RingGeo {
+  static constexpr int esz = FP8 ? 1 : 2;
+  static constexpr int row_bytes = D * esz;
+  static constexpr int chunks = row_bytes / 16;
+  static constexpr int half_bytes = kSub * row_bytes;       // K (or V) rows of one step
+  static constexpr int half_loads = half_bytes / 1024;      // direct loads per half-step
+  static constexpr int wave_bytes = 4 * half_bytes;         // K0, K1, V0, V1
+  static constexpr int ring_bytes = kDecWaves * wave_bytes;
+  static_assert(chunks == 16, "one row is exactly the 16 swizzled chunks");
+  static_assert(ring_bytes + 64 + kPcacheEntries * 4 <= kLdsMax, "LDS budget of the ring");
+};
+
+template <int D, bool FP8, bool RING>
+struct RingBytes { static constexpr int bytes = 0; };
+template <int D, bool FP8>
+struct RingBytes<D, FP8, true> { static constexpr int bytes = RingGeo<D, FP8>::ring_bytes; };
+
 template <int D, bool FP8, int MODE>
 struct Lds {
   using G = Geo<D, FP8>;
-  static constexpr int dec = G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
+  static constexpr int dec = RingDec<D, FP8, MODE>::value
+                                 ? RingBytes<D, FP8, RingDec<D, FP8, MODE>::value>::bytes
+                                 : G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
   static constexpr int pre = (Block<MODE, D>::stream ? G::ring_bufs : 2) * G::tile_bytes;
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
@@ -517,10 +547,13 @@ struct RowMap {
 };
 
 // Write one wave's 32 query rows (columns) starting at packed row r0.  l is
-// already the full row sum (both lane halves).
-template <int D>
-__device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float l_tot, int r0,
-                           const RowMap& rm, int slot, float vdesc, int lane) {
+// already the full row sum (both lane halves).  The wave's accumulator covers
+// head-dim columns [col0, col0 + DS) of rows of width D; the LSE is written
+// only by the wave that owns it (lse_owner).
+template <int D, int DS = D>
+__device__ void write_rows(const AttnParams& p, const SoftmaxState<DS>& st, float l_tot, int r0,
+                           const RowMap& rm, int slot, float vdesc, int lane, int col0 = 0,
+                           bool lse_owner = true) {
   const int r = r0 + (lane & 31);
   const int tok = r / rm.G;
   if (tok >= rm.ntok) return;
@@ -535,11 +568,11 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
     // records; balanced decode slots hold the G rows of one item
     const int64_t row = p.balanced ? (int64_t)slot * rm.G + r
                                    : ((int64_t)slot * p.max_total_q + t) * p.num_q_heads + h;
-    if ((lane >> 5) == 0) p.part_lse[row] = lse2;
+    if (lse_owner && (lane >> 5) == 0) p.part_lse[row] = lse2;
     if (empty) return;
-    float* dst = p.part_o + row * D;
+    float* dst = p.part_o + row * D + col0;
 #pragma unroll
-    for (int tt = 0; tt < D / 32; ++tt)
+    for (int tt = 0; tt < DS / 32; ++tt)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
@@ -549,9 +582,9 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
         *reinterpret_cast<f32x4*>(dst + d0) = v;
       }
   } else {
-    uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D;
+    uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + col0;
 #pragma unroll
-    for (int tt = 0; tt < D / 32; ++tt)
+    for (int tt = 0; tt < DS / 32; ++tt)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
@@ -559,7 +592,7 @@ __device__ void write_rows(const AttnParams& p, const SoftmaxState<D>& st, float
                       pack_bf16x2(st.o[tt][4 * ig + 2] * inv, st.o[tt][4 * ig + 3] * inv)};
         *reinterpret_cast<u32x2*>(dst + d0) = v;
       }
-    if (p.lse && (lane >> 5) == 0) p.lse[(int64_t)t * p.num_q_heads + h] = lse2 * kLn2;
+    if (lse_owner && p.lse && (lane >> 5) == 0) p.lse[(int64_t)t * p.num_q_heads + h] = lse2 * kLn2;
   }
 }
 
@@ -924,6 +957,15 @@ __device__ __forceinline__ void dma_load_16(const uint8_t* src, uint8_t* lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
 }
 
+// Same, with the LDS destination given by its generic address: the low 32
+// bits of a generic pointer into the LDS aperture are the LDS address, which
+// spares the address-space cast (whose null check some inlining contexts
+// could not fold).
+__device__ __forceinline__ void dma_load_16_g(const uint8_t* src, const uint8_t* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
+}
+
 // Workgroup barrier for the ring.  No memory fence: the K/V tiles arrive by
 // direct global->LDS loads whose completion each wave has already waited for
 // (a fence would wait for every load in flight, including the tiles fetched
@@ -1214,6 +1256,222 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
 }
 
 // ---------------------------------------------------------------------------
+// ring decode schedule (fp8 cache, head dim 256): waves split the key range of
+// one block of <= 32 query rows; each wave streams its steps through a private
+// ring of LDS half-step buffers filled by direct global->LDS loads
+// ---------------------------------------------------------------------------
+
+// Direct loads of one half-step (the K or the V rows of 32 keys from key0)
+// into a swizzled buffer: load i fills bytes [1024 i, 1024 i + 1024), lane l
+// the 16 bytes of slot 64 i + l, i.e. row r = (64 i + l) / 16 at chunk
+// position l mod 16, which holds chunk (l mod 16) ^ (r mod 16) of that row.
+// Keys past the live window are clamped to its last key (in bounds; the
+// score mask gives them probability 0).
+template <int D, bool FP8>
+__device__ __forceinline__ void ring_issue(const uint8_t* __restrict__ pool, const PageWalk& w, int key0,
+                                           uint8_t* buf, int lane) {
+  using R = RingGeo<D, FP8>;
+  const int slot_mask = (1 << w.shift) - 1;
+  const int pos = lane & 15;
+  if (w.shift >= 5 && key0 + kSub <= w.kend) {
+    // 32 whole keys on one page (key0 is a multiple of 32): one page id
+    const uint8_t* base = pool + (int64_t)w.pcache[(key0 >> w.shift) - w.first_page] * w.page_bytes +
+                          w.head_off + (uint32_t)(key0 & slot_mask) * (uint32_t)w.row_stride_b;
+#pragma unroll
+    for (int i = 0; i < R::half_loads; ++i) {
+      const int row = 4 * i + (lane >> 4);
+      dma_load_16_g(base + ((uint32_t)row * (uint32_t)w.row_stride_b + (uint32_t)((pos ^ (row & 15)) * 16)),
+                    buf + 1024 * i);
+    }
+    return;
+  }
+  int page[R::half_loads];
+#pragma unroll
+  for (int i = 0; i < R::half_loads; ++i)
+    page[i] = w.pcache[(min(key0 + 4 * i + (lane >> 4), w.kend - 1) >> w.shift) - w.first_page];
+#pragma unroll
+  for (int i = 0; i < R::half_loads; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    const int key = min(key0 + row, w.kend - 1);
+    const uint8_t* src = pool + (int64_t)page[i] * w.page_bytes + w.head_off +
+                         ((uint32_t)(key & slot_mask) * (uint32_t)w.row_stride_b + (uint32_t)((pos ^ (row & 15)) * 16));
+    dma_load_16_g(src, buf + 1024 * i);
+  }
+}
+
+// K operand of k-step j from a swizzled half-step: K[key = kperm(lane%32)][d =
+// 16 j + 8 (lane/32) .. +8] as bf16 (fp8 bytes widened exactly).
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8 k_operand_r(const uint8_t* kl, int j, int lane) {
+  static_assert(FP8, "the ring buffers hold fp8 rows");
+  using R = RingGeo<D, FP8>;
+  const int row = kperm(lane & 31);
+  const u32x2 v = *reinterpret_cast<const u32x2*>(kl + row * R::row_bytes + (j ^ (row & 15)) * 16 + 8 * (lane >> 5));
+  return fp8x8_to_bf16(v[0], v[1]);
+}
+
+// V^T operand of d-tile t, k-step h from a swizzled half-step (the lane
+// mapping of the transposing read is that of v_operand).
+template <int D, bool FP8>
+__device__ __forceinline__ bf16x8 v_operand_r(const uint8_t* vl, int t, int h, int lane) {
+  static_assert(FP8, "the ring buffers hold fp8 rows");
+  using R = RingGeo<D, FP8>;
+  const int L = lane & 15;
+  const int row = 16 * h + 8 * (lane >> 5) + (L >> 1);
+  const int c = (2 * t + ((lane >> 4) & 1)) ^ (row & 15);
+  const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vl + row * R::row_bytes + c * 16 + 8 * (L & 1)));
+  return fp8x8_to_bf16((uint32_t)w[0], (uint32_t)w[1]);
+}
+
+// Merge the softmax states of the NW waves of a workgroup pairwise through
+// LDS (lds_avail bytes from smem): the (m, l, O) of a writer wave is folded
+// into a reader wave with the usual max-rescale; wave 0 ends with the total.
+template <int D, int NW>
+__device__ void merge_waves(SoftmaxState<D>& st, uint8_t* smem, int lds_avail, int wave, int lane) {
+  constexpr int red_floats = D / 2 + 4;               // O registers, then (l, m), per lane
+  const int nbuf = max(1, lds_avail / (red_floats * kWave * 4));
+  float* red = reinterpret_cast<float*>(smem);
+  int active = NW;
+  while (active > 1) {
+    const int half = active / 2;
+    const int cnt = half < nbuf ? half : nbuf;
+    const int w_lo = active - cnt;         // writers [w_lo, active)
+    const int r_lo = active - 2 * cnt;     // readers [r_lo, w_lo)
+    if (wave >= w_lo && wave < active) {
+      f32x4* buf = reinterpret_cast<f32x4*>(red + (wave - w_lo) * red_floats * kWave);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          buf[(4 * t + q) * kWave + lane] = f32x4{st.o[t][4 * q], st.o[t][4 * q + 1], st.o[t][4 * q + 2], st.o[t][4 * q + 3]};
+      buf[(D / 8) * kWave + lane] = f32x4{st.l, st.m, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (wave >= r_lo && wave < w_lo) {
+      const f32x4* buf = reinterpret_cast<const f32x4*>(red + (wave - r_lo) * red_floats * kWave);
+      const f32x4 lm = buf[(D / 8) * kWave + lane];
+      const float mm = fmaxf(st.m, lm[1]);
+      const float ref = mm == neg_inf() ? 0.f : mm;
+      const float a1 = __builtin_amdgcn_exp2f(st.m - ref);
+      const float a2 = __builtin_amdgcn_exp2f(lm[1] - ref);
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = buf[(4 * t + q) * kWave + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.o[t][4 * q + e] = st.o[t][4 * q + e] * a1 + v[e] * a2;
+        }
+      st.l = st.l * a1 + lm[0] * a2;
+      st.m = mm;
+    }
+    __syncthreads();
+    active = w_lo;
+  }
+}
+
+// One (sequence, KV head, key window [klo, khi)) item whose packed query rows
+// fit one MFMA column tile, on an fp8 cache at head dim 256.  Wave w takes the
+// 32-key steps w, w + 4, ... of the window.  Its private LDS holds the K and V
+// rows of two steps; the K rows of step s + 2 are requested as soon as the
+// score product of step s has read its K buffer, the V rows as soon as its PV
+// product has read the V buffer, so about three half-steps (24 KB) per wave
+// are in flight while it computes, with no register holding data in flight
+// and no workgroup barrier in the key loop.  Every step converts each fp8
+// byte once; the four waves' softmax states are merged at the end.
+template <int D, bool FP8, int MODE>
+__device__ void ring_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
+                          const PageWalk& pw, int L, int klo, int khi, int slot, float c, float vdesc) {
+  using R = RingGeo<D, FP8>;
+  constexpr int NW = kDecWaves;
+  constexpr int HL = R::half_loads;
+  const SoftCap sc(p.softcap, c);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nrows = rm.ntok * rm.G;
+
+  if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
+  SoftmaxState<D> st;
+  state_init(st);
+  if (khi <= klo) {
+    if (wave == 0) write_rows<D>(p, st, 0.f, 0, rm, slot, vdesc, lane);
+    return;
+  }
+
+  // query operands of the block's rows (zero past the last row), in registers
+  bf16x8 qreg[D / 16];
+  {
+    const int r = lane & 31;
+    const bool ok = r < nrows;
+    const int tok = ok ? r / rm.G : 0;
+    const int h = rm.g * rm.G + (r - tok * rm.G);
+    const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  const int my_tok = min((lane & 31) / rm.G, max(rm.ntok - 1, 0));
+  const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;   // this lane's row sees keys < klim
+  const int kfull = p.causal ? min(khi, rm.pos0 + 1) : khi;           // keys < kfull visible to every row
+
+  uint8_t* region = smem + wave * R::wave_bytes;       // K0, K1, V0, V1
+  PageWalk w = pw;
+  const int chunk_keys = kPcacheEntries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();                                     // the buffers and page cache are free
+    fill_pcache(w, pcache, cb, ce);
+    // the query loads (first chunk) overlapped the page-table reads; they
+    // retire here, once, so that no wait inside the loop covers them
+    wait_vmem_all();
+    __syncthreads();
+    const int nsteps = (ce - cb + kSub - 1) / kSub;
+    const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;   // this wave's steps
+    if (mine > 0) {
+      // Steps past the wave's last are requested too (clamped to the window's
+      // last key): every iteration then has the same loads in flight and the
+      // same wait counts.
+      auto key_of = [&](int i) { return cb + kSub * min(wave + NW * i, nsteps - 1); };
+      ring_issue<D, FP8>(p.k_pool, w, key_of(0), region, lane);
+      ring_issue<D, FP8>(p.v_pool, w, key_of(0), region + 2 * R::half_bytes, lane);
+      ring_issue<D, FP8>(p.k_pool, w, key_of(1), region + R::half_bytes, lane);
+      ring_issue<D, FP8>(p.v_pool, w, key_of(1), region + 3 * R::half_bytes, lane);
+      for (int i = 0; i < mine; ++i) {
+        const int key0 = cb + kSub * (wave + NW * i);
+        const uint8_t* kl = region + (i & 1) * R::half_bytes;
+        const uint8_t* vl = region + (2 + (i & 1)) * R::half_bytes;
+        wait_vmem<3 * HL>();                             // K(i) landed; V(i), K(i+1), V(i+1) may fly
+        f32x16 sv[1];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sv[0][e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) sv[0] = mfma32(k_operand_r<D, FP8>(kl, j, lane), qreg[j], sv[0]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the K reads have returned
+        ring_issue<D, FP8>(p.k_pool, w, key_of(i + 2), region + (i & 1) * R::half_bytes, lane);
+        if (sc.on()) cap_tile(sv[0], sc);
+        if (key0 + kSub > kfull) mask_tile(sv[0], key0, klim, lane);
+        wait_vmem<3 * HL>();                             // V(i) landed; K(i+1), V(i+1), K(i+2) may fly
+        bf16x8 pb[1][2];
+        softmax_p<D, 1>(st, sv, c, pb);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) st.o[t] = mfma32(v_operand_r<D, FP8>(vl, t, h, lane), pb[0][h], st.o[t]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the V reads have returned
+        ring_issue<D, FP8>(p.v_pool, w, key_of(i + 2), region + (2 + (i & 1)) * R::half_bytes, lane);
+      }
+      wait_vmem_all();                                   // nothing lands in the buffers later
+    }
+  }
+  __syncthreads();
+  merge_waves<D, NW>(st, smem, R::ring_bytes, wave, lane);
+  if (wave == 0) {
+    const float l_tot = st.l + xor32(st.l);
+    write_rows<D>(p, st, l_tot, 0, rm, slot, vdesc, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // the kernel: work-item decode, then one of the schedules
 // ---------------------------------------------------------------------------
 
@@ -1365,7 +1623,10 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
     const int klo = (u - a0) << kUnitShift;
     const int khi = min(L, (pu1 - a0) << kUnitShift);
     const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
-    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
+    if constexpr (RingDec<D, FP8, MODE>::value)
+      ring_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
+    else
+      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
     __syncthreads();                            // LDS is reused by the next piece
     u = pu1;
     ++piece;
@@ -1604,7 +1865,10 @@ void attn_kernel(AttnParams p) {
   const int khi = min(L, klo + p.split_keys);
   const int slot = p.num_splits > 1 ? split : -1;
   if constexpr (MODE == kDecode) {
-    keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
+    if constexpr (RingDec<D, FP8, MODE>::value)
+      ring_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
+    else
+      keysplit_item<D, FP8, MODE>(p, smem, pcache, rm, pw, L, klo, khi, slot, c, vdesc);
   } else if constexpr (MODE == kPrefill) {
     if constexpr (Block<MODE, D>::stream)
       stream_item<D, FP8, MODE, QF8>(p, smem, pcache, rm, pw, L, QF8 ? c * *p.q_descale : c, vdesc);
