@@ -74,7 +74,8 @@ typedef enum {
   PA_ERR_INVALID = -1,      /* bad argument: null/misaligned pointer, bad stride or size */
   PA_ERR_UNSUPPORTED = -2,  /* geometry outside the compiled scope (fail closed) */
   PA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than pa_workspace_bytes() */
-  PA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_SCRATCH = -5       /* pa_run_decode_static: the plan needs more scratch than its static array */
 } pa_status;
 
 typedef enum {
@@ -242,6 +243,25 @@ pa_status pa_run_prefill(pa_plan_t plan, const pa_args* args, hipStream_t stream
  * log-sum-exp merge pass when splits > 1; or, for a balanced plan
  * (num_splits = -1), the balanced persistent schedule and its merge pass. */
 pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream);
+
+/*
+ * Decode without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same computation, kernels and arguments as
+ * pa_run_decode, except that args->workspace and args->workspace_bytes are
+ * ignored: the split partials, balanced-decode records and schedule words live
+ * in a static device array of PA_STATIC_SCRATCH_BYTES (32 MiB) inside
+ * the library, one copy per device, held until the process ends.  The copy of
+ * the current device is used (make the stream's device current); its address
+ * is looked up on the first call on each device.  Nothing is allocated and
+ * nothing needs to start at zero: every word a run reads is written earlier
+ * in the same run.  All calls on one device share the array, so calls that
+ * overlap in time on one device (other streams, other threads) race; serialise
+ * them.  Returns PA_ERR_SCRATCH, with nothing enqueued, when
+ * pa_workspace_bytes(plan) exceeds the array; other errors as pa_run_decode.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_run_decode_static(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /* Unified mixed batch: any mix of q_len_b in one main launch.  Short rows
  * (q_len_b * G <= 32) take the decode schedule, longer ones the prefill

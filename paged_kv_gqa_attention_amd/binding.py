@@ -7,6 +7,7 @@ stream.  The functions keep the C names:
     pa_plan(desc) -> plan            pa_workspace_bytes(plan) -> int
     pa_plan_get_info(plan) -> info   pa_plan_destroy(plan)
     pa_run_prefill / pa_run_decode / pa_run_mixed(plan, args, stream) -> None
+    pa_run_decode_static(plan, args, stream) -> None
     pa_run_append(plan, append_args, stream) -> None
     pa_mla_plan(mla_desc) -> plan    pa_mla_workspace_bytes(plan) -> int
     pa_mla_num_splits(plan) -> int   pa_mla_plan_destroy(plan)
@@ -30,6 +31,8 @@ PA_ERR_INVALID = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_SCRATCH = -5
+PA_STATIC_SCRATCH_BYTES = 32 << 20     # include/pa.h
 
 PA_KV_BF16 = 0
 PA_KV_FP8_E4M3 = 1
@@ -39,7 +42,7 @@ PA_Q_FP8_E4M3 = 1
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
            "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str",
            "pa_mla_plan", "pa_mla_workspace_bytes", "pa_mla_num_splits", "pa_run_mla_decode",
-           "pa_mla_plan_destroy", "pa_check_metadata")
+           "pa_mla_plan_destroy", "pa_check_metadata", "pa_run_decode_static")
 
 PA_CHECK_PAGE_ID = 1
 PA_CHECK_Q_LEN = 2
@@ -181,7 +184,7 @@ def lib():
         L.pa_workspace_bytes.restype = ctypes.c_size_t
         L.pa_plan_get_info.argtypes = [vp, ctypes.POINTER(pa_plan_info)]
         L.pa_plan_get_info.restype = ctypes.c_int
-        for name in ("pa_run_prefill", "pa_run_decode", "pa_run_mixed"):
+        for name in ("pa_run_prefill", "pa_run_decode", "pa_run_mixed", "pa_run_decode_static"):
             f = getattr(L, name)
             f.argtypes = [vp, ctypes.POINTER(pa_args), vp]
             f.restype = ctypes.c_int
@@ -251,6 +254,11 @@ def pa_run_decode(plan, args: pa_args, stream) -> None:
 
 def pa_run_mixed(plan, args: pa_args, stream) -> None:
     _run("pa_run_mixed", plan, args, stream)
+
+
+def pa_run_decode_static(plan, args: pa_args, stream) -> None:
+    """pa_run_decode with the library's static scratch (args' workspace ignored)."""
+    _run("pa_run_decode_static", plan, args, stream)
 
 
 def pa_check_metadata(plan, args: pa_args, flags, stream) -> None:

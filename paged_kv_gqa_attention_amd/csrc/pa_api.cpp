@@ -58,6 +58,8 @@ const char* pa_status_str(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: geometry outside the supported scope";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP runtime or launch failure";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the plan needs more scratch than pa_run_decode_static's static array holds";
   }
   return "unknown pa_status";
 }
@@ -420,6 +422,18 @@ pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream)
 
 pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream) {
   return run(plan, args, stream, pa::kMixed);
+}
+
+pa_status pa_run_decode_static(pa_plan_t plan, const pa_args* args, hipStream_t stream) {
+  if (!plan || !args) return PA_ERR_INVALID;
+  if (plan->d.max_q_len > 1) return PA_ERR_INVALID;
+  if (plan->ws_bytes > pa::kStaticScratchBytes) return PA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (pa::static_scratch(&scratch) != hipSuccess) return PA_ERR_HIP;
+  pa_args a = *args;
+  a.workspace = scratch;
+  a.workspace_bytes = pa::kStaticScratchBytes;
+  return run(plan, &a, stream, pa::kDecode);
 }
 
 }  // extern "C"

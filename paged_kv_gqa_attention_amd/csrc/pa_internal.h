@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "pa.h"
+
 namespace pa {
 
 // Which work decomposition a launch uses.
@@ -148,6 +150,13 @@ hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 
 // Launch the KV-cache append.
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+
+// The allocation-free decode entry point keeps its scratch in a file-scope
+// device array of this many bytes (one copy per device, held until the
+// process ends).  static_scratch returns the current device's copy, looked up
+// once per device with that device current.
+constexpr size_t kStaticScratchBytes = PA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(void** ptr);
 
 // Launch the attention kernel instance for (head_dim, kv dtype, mode).
 hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnParams& p,

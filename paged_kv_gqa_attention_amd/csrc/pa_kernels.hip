@@ -46,9 +46,39 @@
 //     key), page-table columns past the live page count are never read, and
 //     masked scores are selected to -inf, so poisoned cache contents cannot
 //     leak into outputs.
+#include <atomic>
+
 #include "pa_internal.h"
 
+// Scratch of pa_run_decode_static (split partials, balanced-decode records
+// and their schedule words): a file-scope device array, one copy per device.
+// In host code this name is only a stand-in for the symbol; kernels receive
+// the device address that static_scratch looks up.
+static __device__ __align__(256) unsigned char scratch[pa::kStaticScratchBytes];
+
 namespace pa {
+
+// Device address of `scratch` on the current device, resolved with
+// hipGetSymbolAddress the first time each device asks and kept afterwards
+// (every device holds its own copy at its own address).
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -45,9 +45,33 @@ def plan_status(**kw):
 
 
 def test_status_strings():
-    for code in (B.PA_OK, B.PA_ERR_INVALID, B.PA_ERR_UNSUPPORTED, B.PA_ERR_WORKSPACE, B.PA_ERR_HIP):
+    for code in (B.PA_OK, B.PA_ERR_INVALID, B.PA_ERR_UNSUPPORTED, B.PA_ERR_WORKSPACE, B.PA_ERR_HIP,
+                 B.PA_ERR_SCRATCH):
         assert B.pa_status_str(code).startswith("PA_")
     assert "unknown" in B.pa_status_str(-99)
+
+
+def test_static_decode_host_checks():
+    # the allocation-free decode refuses, before touching any device, a plan
+    # whose scratch exceeds its static array, a NULL plan or arguments, and a
+    # plan with more than one query token per sequence
+    p = B.pa_plan(desc(num_seqs=4, num_q_heads=64, num_kv_heads=2, head_dim=256, page_size=128,
+                       page_table_cols=64, max_total_q=4096, max_seq_len=8192,
+                       kv_dtype=B.PA_KV_FP8_E4M3, num_splits=4))
+    try:
+        assert B.pa_workspace_bytes(p) > B.PA_STATIC_SCRATCH_BYTES
+        a = B.pa_args()
+        assert B.lib().pa_run_decode_static(p, ctypes.byref(a), None) == B.PA_ERR_SCRATCH
+        assert B.lib().pa_run_decode_static(p, None, None) == B.PA_ERR_INVALID
+        assert B.lib().pa_run_decode_static(None, ctypes.byref(a), None) == B.PA_ERR_INVALID
+    finally:
+        B.pa_plan_destroy(p)
+    p = B.pa_plan(desc(max_q_len=2, max_total_q=8))
+    try:
+        a = B.pa_args()
+        assert B.lib().pa_run_decode_static(p, ctypes.byref(a), None) == B.PA_ERR_INVALID
+    finally:
+        B.pa_plan_destroy(p)
 
 
 @pytest.mark.parametrize("kw,code", [
