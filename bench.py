@@ -266,15 +266,15 @@ def oracle_check_mla(w, out, lse, n=96):
 
 def oracle_check(w, out, lse, rows):
     """Compare sampled output rows with the fp64 oracle's."""
-    from tests import helpers as H
-    return validate(w, out, lse, rows, H.run_oracle(w, rows=rows))
+    import oracle
+    return validate(w, out, lse, rows, oracle.attention_workload(w, rows=rows))
 
 
 def cpu_baseline(w, budget_s=10.0):
     """The oracle, untuned, on a bounded sample: groups of 16 whole sequences
     (all heads), in order and wrapping round, until about budget_s seconds of
     work; reports KV GB/s over the sample."""
-    from tests import helpers as H
+    import oracle
     Hq = w.num_q_heads
     cu = w.cu_q_lens.numpy()
     L = w.seq_lens.numpy().astype(np.int64)
@@ -285,7 +285,7 @@ def cpu_baseline(w, budget_s=10.0):
         take = min(w.num_seqs - b, 16)
         rows = np.arange(cu[b] * Hq, cu[b + take] * Hq, dtype=np.int64)
         t = time.time()
-        H.run_oracle(w, rows=rows, threads=threads)
+        oracle.attention_workload(w, rows=rows, threads=threads)
         elapsed += time.time() - t
         done_bytes += int(L[b:b + take].sum()) * w.num_kv_heads * w.head_dim * 2 * \
             (2 if w.kv_dtype == "bf16" else 1)
@@ -372,7 +372,10 @@ def main():
     sec = {}
     if not a.no_secondary:
         for name in ("prefill_causal", "mixed_24b", "decode_fp8_long"):
-            r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup, cpu_leg)
+            # the prefill's CPU check covers 8 tokens x 8 heads of every sequence
+            rp = (8, 8) if name == "prefill_causal" else (2, 2)
+            r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup, cpu_leg,
+                               sample_rows_per_seq=rp[0], heads=rp[1])
             bound = "mfma" if name == "prefill_causal" else "hbm"
             if bound == "mfma":
                 frac = r["tflops"] / BF16_PEAK_TFLOPS

@@ -206,6 +206,44 @@ def attention(*, q_bits: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     return out, lse
 
 
+def workload_arrays(w):
+    """numpy views of a workload object (anything with the attributes of the
+    seeded workloads: q, k_pool, v_pool as torch CPU tensors, kv_dtype and
+    q_dtype names): q as bf16 bits or E4M3 codes, K/V pools as bf16 bits or
+    fp8 bytes.  Marshalling only."""
+    import torch
+    if w.q.dtype == torch.uint8:                      # fp8 queries: E4M3 codes
+        q = w.q.contiguous().numpy()
+    else:
+        q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    if w.kv_dtype == "bf16":
+        k = w.k_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
+        v = w.v_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
+    else:
+        k = w.k_pool.contiguous().numpy()
+        v = w.v_pool.contiguous().numpy()
+    return q, k, v
+
+
+def attention_workload(w, rows=None, key_begin=0, key_end=-1, causal=None, scale=None,
+                       threads=0, softcap=None):
+    """attention() over a workload object's tensors and metadata (argument
+    marshalling only; see workload_arrays)."""
+    q, k, v = workload_arrays(w)
+    return attention(
+        q_bits=q, k_pool=k, v_pool=v, page_table=w.page_table.numpy(),
+        cu_q_lens=w.cu_q_lens.numpy(), seq_lens=w.seq_lens.numpy(),
+        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+        page_size=w.page_size, scale=w.scale if scale is None else scale,
+        causal=w.causal if causal is None else causal,
+        kv_dtype=KV_BF16 if w.kv_dtype == "bf16" else KV_FP8_E4M3,
+        k_descale=w.k_descale, v_descale=w.v_descale, rows=rows,
+        key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads,
+        softcap=w.softcap if softcap is None else softcap,
+        q_dtype=Q_FP8_E4M3 if w.q_dtype == "fp8_e4m3" else Q_BF16,
+        q_descale=w.q_descale)
+
+
 def merge(o_parts: np.ndarray, lse_parts: np.ndarray):
     """Combine partials over disjoint key windows: o_parts [S, n, D], lse_parts [S, n]."""
     o_parts = _c(o_parts, np.float64)

@@ -15,34 +15,45 @@ from paged_kv_gqa_attention_amd import synth
 
 def bits(w: synth.Workload):
     """numpy views of a workload: q bf16 bits, K/V pools (bf16 bits or fp8 bytes)."""
-    if w.q.dtype == torch.uint8:                      # fp8 queries: E4M3 codes
-        q = w.q.contiguous().numpy()
-    else:
-        q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
-    if w.kv_dtype == "bf16":
-        k = w.k_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
-        v = w.v_pool.contiguous().view(torch.int16).numpy().view(np.uint16)
-    else:
-        k = w.k_pool.contiguous().numpy()
-        v = w.v_pool.contiguous().numpy()
-    return q, k, v
+    return oracle.workload_arrays(w)
 
 
 def run_oracle(w: synth.Workload, rows=None, key_begin=0, key_end=-1, causal=None,
                scale=None, threads=0, softcap=None):
-    q, k, v = bits(w)
-    return oracle.attention(
-        q_bits=q, k_pool=k, v_pool=v, page_table=w.page_table.numpy(),
-        cu_q_lens=w.cu_q_lens.numpy(), seq_lens=w.seq_lens.numpy(),
-        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
-        page_size=w.page_size, scale=w.scale if scale is None else scale,
-        causal=w.causal if causal is None else causal,
-        kv_dtype=oracle.KV_BF16 if w.kv_dtype == "bf16" else oracle.KV_FP8_E4M3,
-        k_descale=w.k_descale, v_descale=w.v_descale, rows=rows,
-        key_begin=key_begin, key_end=key_end, pt_cols=w.pt_cols, threads=threads,
-        softcap=w.softcap if softcap is None else softcap,
-        q_dtype=oracle.Q_FP8_E4M3 if w.q_dtype == "fp8_e4m3" else oracle.Q_BF16,
-        q_descale=w.q_descale)
+    return oracle.attention_workload(w, rows=rows, key_begin=key_begin, key_end=key_end,
+                                     causal=causal, scale=scale, threads=threads,
+                                     softcap=softcap)
+
+
+def cover_rows(w: synth.Workload, q_block_tokens: int, seed: int = 5):
+    """Flat (t*Hq + h) rows that touch every work item of a launch: for each
+    sequence, each q-block of q_block_tokens query tokens and each slice of
+    32 // G tokens inside it (the packed rows one wave owns), one random token
+    with one random query head of every KV head; plus each sequence's first
+    and last query token at every head.  Sequences with q_len * G <= 32 (one
+    wave's rows) contribute all their rows."""
+    rng = np.random.default_rng(seed)
+    cu = w.cu_q_lens.numpy()
+    Hq, Hkv = w.num_q_heads, w.num_kv_heads
+    G = Hq // Hkv
+    per_wave = max(1, 32 // G)
+    rows = set()
+    for b in range(w.num_seqs):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi <= lo:
+            continue
+        if (hi - lo) * G <= 32:
+            rows.update(t * Hq + h for t in range(lo, hi) for h in range(Hq))
+            continue
+        for t in (lo, hi - 1):
+            rows.update(t * Hq + h for h in range(Hq))
+        for q0 in range(lo, hi, q_block_tokens):
+            q1 = min(hi, q0 + q_block_tokens)
+            for s0 in range(q0, q1, per_wave):
+                t = int(rng.integers(s0, min(q1, s0 + per_wave)))
+                for g in range(Hkv):
+                    rows.add(t * Hq + g * G + int(rng.integers(0, G)))
+    return sorted(rows)
 
 
 def decoded_pools(w: synth.Workload):

@@ -1,7 +1,10 @@
 """GPU parity at full size: the four large workloads in the launch configuration
 bench.py times (plus the other entry points that accept them), compared with
-the oracle on sampled rows -- every sequence's first and last query token and
-random ones, each with several query heads."""
+the oracle element by element.  The decode workloads are checked on every
+row; the prefill and the serving mix on rows that touch every work item of
+the launch (each q-block, each wave's token slice, each KV head) plus every
+sequence's first and last token at every head; other schedules on sampled
+rows."""
 import numpy as np
 import pytest
 import torch
@@ -26,30 +29,49 @@ def run_sampled(w, mode, num_splits=0, per_seq=3, heads=4):
                  what="%s/%s/S%d" % (w.name, mode, pa.info.num_splits))
 
 
+def run_rows(w, mode, rows, num_splits=0):
+    """One run of the bench launch configuration, checked on `rows` (None:
+    every row)."""
+    print("case", w.name, mode, "splits", num_splits, "rows", "all" if rows is None else len(rows),
+          flush=True)
+    x = DeviceInputs(w)
+    pa = PagedAttention(w, num_splits=num_splits)
+    out, lse = pa.run(mode, x)
+    torch.cuda.synchronize()
+    ref = H.run_oracle(w, rows=rows)
+    return check(w, out, lse, ref[0], ref[1], rows=rows,
+                 what="%s/%s/S%d" % (w.name, mode, pa.info.num_splits)), pa
+
+
 def test_decode_llama8b_full():
     w = synth.decode_llama8b()
-    run_sampled(w, "decode")
+    run_rows(w, "decode", None)                   # every row
     run_sampled(w, "decode", num_splits=3)
     run_sampled(w, "mixed")
 
 
 def test_prefill_causal_full():
     w = synth.prefill_causal()
-    run_sampled(w, "prefill", per_seq=6)
+    pa = PagedAttention(w)
+    rows = H.cover_rows(w, pa.info.q_block_tokens)
+    assert len(rows) > 30000
+    run_rows(w, "prefill", rows)                  # every (q-block, wave slice, KV head)
     run_sampled(w, "mixed", per_seq=6)
 
 
 def test_mixed_24b_full():
     w = synth.mixed_24b()
-    run_sampled(w, "mixed", per_seq=4)
+    pa = PagedAttention(w)
+    rows = H.cover_rows(w, pa.info.mixed_q_block_tokens)
+    run_rows(w, "mixed", rows)                    # every queue item, every decode row
     run_sampled(w, "prefill", per_seq=4)
     ws = synth.mixed_24b(shuffle=True)
-    run_sampled(ws, "mixed", per_seq=4)
+    run_rows(ws, "mixed", H.cover_rows(ws, pa.info.mixed_q_block_tokens))
 
 
 def test_decode_fp8_long_full():
     w = synth.decode_fp8_long()
-    run_sampled(w, "decode", heads=8)
+    run_rows(w, "decode", None)                   # every row (balanced schedule)
     run_sampled(w, "decode", num_splits=1, heads=8)
     run_sampled(w, "mixed", heads=8)
 
@@ -57,7 +79,7 @@ def test_decode_fp8_long_full():
 def test_full_size_outputs_are_finite_everywhere():
     # every row, not just the sample: poisoned tails never leak
     for make, mode in ((synth.decode_llama8b, "decode"), (synth.decode_fp8_long, "decode"),
-                       (synth.mixed_24b, "mixed")):
+                       (synth.mixed_24b, "mixed"), (synth.prefill_causal, "prefill")):
         w = make()
         x = DeviceInputs(w)
         pa = PagedAttention(w)

@@ -144,13 +144,13 @@ def test_split_heuristic_and_workspace():
     info = B.pa_plan_get_info(p)
     assert info.balanced_workgroups == 2 * 256 and info.num_splits == 1
     assert B.pa_workspace_bytes(p) >= 2 * 512 * 4 * (128 + 1) * 4
-    B.pa_plan_destroy(p)
-    assert plan_status(num_splits=-2) == B.PA_ERR_INVALID
     # -1 also puts mixed runs on the task queues: one workgroup per resident
     # slot of the mixed kernel (two per CU at D 128 bf16); the workspace holds
     # 2 counters, 1024 arrival counters and two offset lists of B + 1
     assert info.queue_workgroups == 2 * 256
     assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 257) * 4
+    B.pa_plan_destroy(p)
+    assert plan_status(num_splits=-2) == B.PA_ERR_INVALID
     p = B.pa_plan(desc(num_seqs=4096, page_table_cols=16, max_total_q=4096, num_splits=-1))
     assert B.pa_plan_get_info(p).queue_workgroups == 512
     assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 4097) * 4
