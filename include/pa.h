@@ -221,12 +221,17 @@ typedef struct {
 /* Validate a shape description and build a plan.  Host only; uses the HIP
  * runtime only when desc->num_cus == 0.  Returns PA_ERR_INVALID for malformed
  * descriptions and PA_ERR_UNSUPPORTED for geometry outside the compiled scope;
- * *out is set only on PA_OK. */
+ * *out is set only on PA_OK.  One plan per batch shape, metadata bound at run
+ * time, unsupported requests refused so the caller can fall back: TensorRT-LLM
+ * PR #17399, "Planning, preprocessing, and workspace ownership" and
+ * "Integration and supported scope". */
 pa_status pa_plan(const pa_desc* desc, pa_plan_t* out);
 
 /* Bytes of workspace a run of this plan needs (0 when no split is used).
  * Prefill runs need none; decode and mixed runs need this much when the plan
- * splits the key range. Returns 0 for a NULL plan. */
+ * splits the key range. Returns 0 for a NULL plan.  The caller owns and
+ * aligns the workspace, context (prefill) runs need none: TensorRT-LLM PR
+ * #17399, "Planning, preprocessing, and workspace ownership". */
 size_t pa_workspace_bytes(pa_plan_t plan);
 
 /* Fill *info with the plan's choices. */
@@ -235,13 +240,18 @@ pa_status pa_plan_get_info(pa_plan_t plan, pa_plan_info* info);
 /* Varlen prefill (any q_len_b <= seq_lens[b], including chunked prefill on
  * cached keys): query heads of one KV head packed into bf16 MFMA tiles, K/V
  * tiles shared through LDS, online softmax.  Never splits the key range and
- * needs no workspace. */
+ * needs no workspace.  The paged prefill specialisation of vLLM PR #48156
+ * (summary and kernel micro-benchmark table), with the varlen GQA packing of
+ * vLLM PR #16828 (description). */
 pa_status pa_run_prefill(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /* Decode: at most one query token per sequence (token b of sequence b when
- * cu_q_lens is NULL).  Split-KV over the plan's num_splits windows, then a
- * log-sum-exp merge pass when splits > 1; or, for a balanced plan
- * (num_splits = -1), the balanced persistent schedule and its merge pass. */
+ * cu_q_lens is NULL).  Split-KV over the plan's num_splits windows (the last
+ * window takes every key past the others), then a log-sum-exp merge pass when
+ * splits > 1; or, for a balanced plan (num_splits = -1), the balanced
+ * persistent schedule and its merge pass.  The paged decode with split-KV of
+ * vLLM PR #48156 (split-KV discussion) over the page-table metadata of
+ * TensorRT-LLM PR #17399 ("Unified page-table metadata"). */
 pa_status pa_run_decode(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /*
@@ -268,7 +278,8 @@ pa_status pa_run_decode_static(pa_plan_t plan, const pa_args* args, hipStream_t 
  * schedule, both inside the same kernel; split-KV and the merge pass as for
  * decode.  A plan with num_splits = -1 runs the task-queue schedule instead
  * (a one-workgroup setup launch that lays out the queues in the workspace,
- * then the persistent main launch; no merge). */
+ * then the persistent main launch; no merge).  One kernel for any query
+ * length: vLLM PR #16828 (description, "Further benchmarking"). */
 pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream);
 
 /*
@@ -291,9 +302,10 @@ pa_status pa_run_mixed(pa_plan_t plan, const pa_args* args, hipStream_t stream);
  *                 even mantissa, saturating at +-448 (NaN gives the NaN code, sign kept)
  * Uses the plan's geometry (B, Hkv, D, page size, pool layout, KV dtype); Hq,
  * splits and the workspace play no part.  Nothing else in the pools changes.
- * A token whose position falls outside 0 .. page_table_cols * page - 1, or whose
- * row is at or past max_total_q, breaks the contract and is skipped (the lengths
- * live on the device, so no status reports it).  All buffers stay the caller's;
+ * A token whose position falls outside 0 .. page_table_cols * page - 1, whose
+ * page id lies outside [0, num_pages), or whose row is at or past max_total_q,
+ * breaks the contract and is skipped (the metadata lives on the device, so no
+ * status reports it).  All buffers stay the caller's;
  * the library keeps no pointer past the call.  Asynchronous on `stream`; host-side
  * errors as for the runs (PA_ERR_INVALID for a NULL or misaligned pointer, a
  * stride below Hkv*D or not a multiple of 8, missing fp8 descales).
@@ -341,7 +353,9 @@ enum {
 };
 pa_status pa_check_metadata(pa_plan_t plan, const pa_args* args, int32_t* flags, hipStream_t stream);
 
-/* Release a plan (NULL is ignored). */
+/* Release a plan (NULL is ignored).  The plan is the caller's host object,
+ * built once per batch shape (TensorRT-LLM PR #17399, "Planning,
+ * preprocessing, and workspace ownership"). */
 void pa_plan_destroy(pa_plan_t plan);
 
 /*

@@ -129,9 +129,11 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
     const int64_t by_len = std::max<int64_t>(1, max_len / kMinSplitKeys);
     splits = (int)std::max<int64_t>(1, std::min(want, by_len));
   }
-  int64_t split_keys = capacity > 0 ? ceil_div(capacity, splits) : kSplitAlign;
+  // windows laid over the longest live sequence the plan expects; the last
+  // window takes every key past the others (longer sequences stay correct)
+  int64_t split_keys = max_len > 0 ? ceil_div(max_len, splits) : kSplitAlign;
   split_keys = std::max<int64_t>(kSplitAlign, ceil_div(split_keys, kSplitAlign) * kSplitAlign);
-  splits = (int)std::max<int64_t>(1, capacity > 0 ? ceil_div(capacity, split_keys) : 1);
+  splits = (int)std::max<int64_t>(1, max_len > 0 ? ceil_div(max_len, split_keys) : 1);
   p->num_splits = splits;
   p->split_keys = (int32_t)split_keys;
   if (splits > 1) {
@@ -245,6 +247,7 @@ pa_status pa_run_append(pa_plan_t plan, const pa_append_args* a, hipStream_t str
   p.fp8 = fp8 ? 1 : 0;
   p.k_descale = fp8 ? a->k_descale : nullptr;
   p.v_descale = fp8 ? a->v_descale : nullptr;
+  p.num_pages = d.num_pages;
   return pa::launch_append(p, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

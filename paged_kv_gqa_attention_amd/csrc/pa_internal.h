@@ -108,6 +108,7 @@ struct AppendParams {
   int32_t fp8;
   const float* k_descale;
   const float* v_descale;
+  int32_t num_pages;            // page ids outside [0, num_pages) are not written through
 };
 
 struct BalancedMergeParams {

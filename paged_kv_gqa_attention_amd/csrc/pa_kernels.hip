@@ -840,7 +840,8 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   wait_vmem_all();
 
   const int klo = split * p.split_keys;
-  int khi = min(L, klo + p.split_keys);
+  // the last window takes every remaining key
+  int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
   if (p.causal) khi = min(khi, rm.pos0 + rm.ntok);
 
   // visibility: the wave's rows are tokens [tok_a, tok_b]; lane rows per column tile
@@ -1892,7 +1893,7 @@ void attn_kernel(AttnParams p) {
   float c, vdesc;
   score_scales<FP8>(p, c, vdesc);
   const int klo = split * p.split_keys;
-  const int khi = min(L, klo + p.split_keys);
+  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);   // the last window takes the rest
   const int slot = p.num_splits > 1 ? split : -1;
   if constexpr (MODE == kDecode) {
     if constexpr (RingDec<D, FP8, MODE>::value)
@@ -2784,7 +2785,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       if (pos >= 0 && pos < (p.pt_cols << p.page_shift)) {
         const int page = p.page_table[(int64_t)lo * p.pt_row_stride + (pos >> p.page_shift)];
         const int slot = pos & ((1 << p.page_shift) - 1);
-        off = (int64_t)page * p.kv_page_bytes + (int64_t)slot * p.num_kv_heads * p.head_dim * esz;
+        // a page id outside the pool is a contract violation: the row is skipped
+        if (page >= 0 && page < p.num_pages)
+          off = (int64_t)page * p.kv_page_bytes + (int64_t)slot * p.num_kv_heads * p.head_dim * esz;
       }
     }
     row_off[threadIdx.x] = off;

@@ -178,6 +178,42 @@ def test_contract_violations_and_row_cap_write_nothing():
     assert_pools_equal(x, ko, vo, "contract violations")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_page_ids_outside_the_pool_are_not_written(kv):
+    # sequence 1's last live page-table column names a page past the pool (or
+    # -1): the new rows that land there are skipped, every other row lands
+    w = H.random_workload(410 + (kv == "fp8_e4m3"), kv_dtype=kv, B=3, max_len=90, decode=False)
+    ql = w.q_lens.astype(np.int64)
+    L = w.seq_lens.numpy().astype(np.int64)
+    k_new, v_new = new_rows(w, 7, spread=False)
+    col = int((L[1] - 1) // w.page_size)
+    for bad in (w.num_pages + 7, -1):
+        print("append bad page id", bad, kv, flush=True)
+        x = DeviceInputs(w)
+        x.page_table[1, col] = bad
+        pa = PagedAttention(w)
+        a = B.make_append_args(k_new=k_new.cuda(), v_new=v_new.cuda(), cu_new=x.cu_q_lens,
+                               seq_lens=x.seq_lens, page_table=x.page_table, k_pool=x.k_pool,
+                               v_pool=x.v_pool, k_descale=x.k_descale, v_descale=x.v_descale)
+        B.pa_run_append(pa.plan, a, B.current_stream())
+        torch.cuda.synchronize()
+        # expected: sequence 1 without its new rows on that page (they are its
+        # last ones, so the others keep their positions)
+        cu = w.cu_q_lens.numpy()
+        pos = L[1] - ql[1] + np.arange(ql[1])
+        drop = int(np.sum(pos // w.page_size == col))
+        keep = np.ones(w.total_q, dtype=bool)
+        keep[cu[2] - drop:cu[2]] = False
+        exp_L = L.copy()
+        exp_L[1] -= drop
+        kept_ql = np.array([int(np.sum(keep[cu[b]:cu[b + 1]])) for b in range(w.num_seqs)])
+        cu2 = np.concatenate([[0], np.cumsum(kept_ql)]).astype(np.int32)
+        idx = torch.from_numpy(np.nonzero(keep)[0])
+        ko, vo = oracle_append(w, k_new[idx], v_new[idx], cu_new=cu2, seq_lens=exp_L.astype(np.int32))
+        assert drop > 0
+        assert_pools_equal(x, ko, vo, "page id %d" % bad)
+
+
 @pytest.mark.parametrize("descale", [1.0, 0.125, 0.0123, 3.7])
 def test_fp8_encoder_every_bf16_value(descale):
     # every bf16 bit pattern (NaN payloads, infinities, subnormals, both zeros)

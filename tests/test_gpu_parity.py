@@ -100,3 +100,21 @@ def test_random_decode(seed):
     for s in (0, 1, 2, 5):
         run_and_check(w, "decode", num_splits=s, ref=ref)
     run_and_check(w, "mixed", ref=ref)
+
+
+@pytest.mark.parametrize("mode", ["decode", "mixed"])
+def test_sequences_longer_than_the_planned_max(mode):
+    # the plan's split windows cover max_seq_len = 1024; sequences run to
+    # about 3,000 keys, so the last window takes every key past 768
+    L = [3000, 1024, 1500, 7, 2049]
+    w = synth.build(name="past_max_" + mode, seq_lens=L, q_lens=[1] * 5, num_q_heads=16,
+                    num_kv_heads=4, head_dim=128, page_size=16, seed=61, threads=1)
+    ref = H.run_oracle(w)
+    for splits in (3, 4):
+        pa = PagedAttention(w, num_splits=splits, max_seq_len=1024)
+        print("case", w.name, "splits", pa.info.num_splits, "window", pa.info.split_keys, flush=True)
+        assert (pa.info.num_splits - 1) * pa.info.split_keys < 1024   # the last window starts inside
+        x = DeviceInputs(w)
+        out, lse = pa.run(mode, x)
+        torch.cuda.synchronize()
+        check(w, out, lse, ref[0], ref[1], what="%s/S%d" % (w.name, splits))

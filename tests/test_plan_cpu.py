@@ -163,6 +163,15 @@ def test_split_heuristic_and_workspace():
     info = B.pa_plan_get_info(p)
     assert info.num_splits == 3 and info.split_keys == 384
     B.pa_plan_destroy(p)
+    # the windows cover max_seq_len, not the page-table capacity (256 pages of
+    # 16 keys here): every window holds live keys
+    p = B.pa_plan(desc(num_splits=4, page_table_cols=256, max_seq_len=1024))
+    info = B.pa_plan_get_info(p)
+    assert info.num_splits == 4 and info.split_keys == 256
+    B.pa_plan_destroy(p)
+    p = B.pa_plan(desc(num_splits=4, page_table_cols=256, max_seq_len=0))   # 0: the capacity
+    assert B.pa_plan_get_info(p).split_keys == 1024
+    B.pa_plan_destroy(p)
 
 
 def test_prefill_block_shape():
