@@ -38,8 +38,9 @@ METRIC = "paged-attn prefill TFLOP/s + decode KV GB/s, as % of MI355X roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 FP8_PEAK_TFLOPS = 2 * BF16_PEAK_TFLOPS
-# half the flops at each rate (q.k on fp8, p.v on bf16): 1 / (0.5/fp8 + 0.5/bf16)
-FP8Q_PEAK_TFLOPS = 1.0 / (0.5 / FP8_PEAK_TFLOPS + 0.5 / BF16_PEAK_TFLOPS)
+# fp8 queries on an fp8 cache: q.k and (on the tiles every row of a wave sees)
+# p.v run on the E4M3 matrix cores, so the roof is the dense fp8 peak
+FP8Q_PEAK_TFLOPS = FP8_PEAK_TFLOPS
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_gqa_attention_amd", "csrc", "pa_kernels.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
@@ -399,8 +400,8 @@ def main():
                                                        e["roofline_frac"]),
               file=sys.stderr, flush=True)
         # fp8 cache, bf16 queries vs fp8 queries: the second runs its score
-        # product on the E4M3 matrix cores (5.0 PFLOP/s dense) and P.V in bf16
-        # (2.5), so its peak is the harmonic mean of the halves, 3.33 PFLOP/s
+        # product and (off the diagonal) its PV product on the E4M3 matrix
+        # cores, so it is measured against the dense fp8 peak (5.03 PFLOP/s)
         for qd in ("bf16", "fp8_e4m3"):
             r = bench_workload("prefill_causal", "prefill", max(5, a.steps // 2), a.warmup, cpu_leg,
                                kv_dtype="fp8_e4m3", q_dtype=qd)

@@ -109,7 +109,7 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   p->page_shift = ilog2(d.page_size);
   p->esz = esz;
   p->num_cus = cus;
-  p->q_block_tokens = std::max(1, pa::block_rows(d.head_dim, pa::kPrefill) / G);
+  p->q_block_tokens = std::max(1, pa::block_rows(d.head_dim, pa::kPrefill, d.q_dtype == PA_Q_FP8_E4M3) / G);
   p->mixed_q_block_tokens = std::max(1, pa::block_rows(d.head_dim, pa::kMixed) / G);
   p->kv_page_bytes = page_elems * esz;
   p->rows_cap = std::max(d.max_total_q, d.num_seqs);

@@ -170,7 +170,7 @@ int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode);
 // (by LDS and by waves per SIMD).
 int workgroups_per_cu(int head_dim, bool kv_fp8, Mode mode);
 // Packed query rows (tokens x GQA heads) per workgroup of a launch mode.
-int block_rows(int head_dim, Mode mode);
+int block_rows(int head_dim, Mode mode, bool q_fp8 = false);
 
 }  // namespace pa
 

@@ -95,7 +95,9 @@ constexpr int kDecWaves = 4;              // waves per workgroup, decode and mix
 // (168 VGPRs; measured 6-9 % faster than two per SIMD, the third wave hiding
 // LDS and MFMA dependency latency), two at head dim 64 (whose fp8 tile has
 // fewer direct loads than twelve waves)
-constexpr int stream_waves(int D) { return D == 128 ? 12 : 8; }
+// (with fp8 queries, whose E4M3 PV product keeps more state per wave, two
+// per SIMD at head dim 128 as well)
+constexpr int stream_waves(int D, bool qf8) { return D == 128 && !qf8 ? 12 : 8; }
 
 // Workgroup shape of a launch.  Decode and mixed workgroups have 4 waves so
 // that two of them share a compute unit and one's prologue/epilogue overlaps
@@ -103,10 +105,10 @@ constexpr int stream_waves(int D) { return D == 128 ? 12 : 8; }
 // schedule: 12 or 8 waves, one workgroup per compute unit, all of LDS a ring
 // of K/V tiles.  Head dim 256 keeps a 128-row fp32 accumulator per wave, so
 // its workgroups run one wave per SIMD with the accumulator in AGPRs.
-template <int MODE, int D>
+template <int MODE, int D, bool QF8 = false>
 struct Block {
   static constexpr bool stream = MODE == kPrefill && D <= 128;
-  static constexpr int waves = stream ? stream_waves(D) : kDecWaves;
+  static constexpr int waves = stream ? stream_waves(D, QF8) : kDecWaves;
   static constexpr int threads = waves * kWave;
   // prefill schedule: 32-row MFMA column tiles per wave (a second tile would
   // share every K/V operand read, but its accumulator costs the occupancy that
@@ -202,7 +204,11 @@ struct Lds {
   static constexpr int dec = RingDec<D, FP8, MODE>::value
                                  ? RingBytes<D, FP8, RingDec<D, FP8, MODE>::value>::bytes
                                  : G::q_bytes + G::template DecWaves<Block<MODE, D>::waves>::value * G::stage_bytes;
-  static constexpr int pre = (Block<MODE, D>::stream ? G::ring_bufs : 2) * G::tile_bytes;
+  // streamed prefill of an fp8 cache: the ring, then room for the E4M3 query
+  // rows of every wave when the queries are fp8 (q8_pitch bytes per row)
+  static constexpr int q8_pitch = D + 16;
+  static constexpr int q8_off = (Block<MODE, D>::stream ? G::ring_bufs : 2) * G::tile_bytes;
+  static constexpr int pre = q8_off + (Block<MODE, D>::stream && FP8 ? Block<MODE, D, true>::waves * kCols * q8_pitch : 0);
   static constexpr int base = MODE == kDecode ? dec : (MODE == kPrefill ? pre : CMax<dec, pre>::value);
   static constexpr int meta = 64;                      // work-item metadata words
   static constexpr int pcache_entries = kPcacheEntries;
@@ -399,6 +405,14 @@ __device__ __forceinline__ i32x8 k_operand_f8(const uint8_t* kl, int kb, int j, 
   return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
+// E4M3 query operand of the 64-wide k-step j from this lane's query row in
+// LDS (qrow already offset by 32 bytes for lanes >= 32): 32 bytes.
+__device__ __forceinline__ i32x8 q8_operand(const uint8_t* qrow, int j) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(qrow + 64 * j);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(qrow + 64 * j + 16);
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -494,7 +508,7 @@ constexpr float kRescaleSlack = 8.0f;
 // accumulator when the row max grew by more than the slack, and returns the
 // probabilities as bf16 PV B-operands.  c = softmax_scale * log2(e) (*
 // k_descale), c > 0.
-template <int D, int NS>
+template <int D, int NS, bool INT_M = false>
 __device__ __forceinline__ void max_update(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c) {
   float mx = neg_inf();
 #pragma unroll
@@ -504,7 +518,9 @@ __device__ __forceinline__ void max_update(SoftmaxState<D>& st, const f32x16 (&s
   mx = fmaxf(mx, xor32(mx));
   const float mxs = mx * c;
   if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m, mxs);
+    // INT_M: the reference is rounded up to an integer, so that every rescale
+    // factor is a power of two
+    const float m_new = INT_M ? __builtin_ceilf(fmaxf(st.m, mxs)) : fmaxf(st.m, mxs);
     const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
     st.l *= alpha;
 #pragma unroll
@@ -1102,11 +1118,13 @@ struct QOp<true> {
   template <int D> struct n { static constexpr int value = D / 64; };
 };
 
+// With fp8 queries (QF8) the query operands are read from the wave's rows in
+// LDS (qrow: this lane's row, 16-byte aligned) instead of qreg.
 template <int D, bool FP8, int KPITCH, int VPITCH, bool QF8>
 __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
                                             const uint8_t* kl, const uint8_t* vl,
                                             const typename QOp<QF8>::reg (&qreg)[QOp<QF8>::template n<D>::value],
-                                            float c, int lane) {
+                                            const uint8_t* qrow, float c, int lane) {
   constexpr int NQ = QOp<QF8>::template n<D>::value;   // score MFMAs (k-steps over the head dim)
   constexpr int NT = D / 32;            // 32-wide d tiles of O
   constexpr int NV = 2 * NT;            // PV MFMAs; operand v = (tile v % NT, half v / NT)
@@ -1134,7 +1152,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     fetch(j + 2);
-    if constexpr (QF8) sn = mfma32_f8(ka[j], qreg[j], sn);
+    if constexpr (QF8) sn = mfma32_f8(ka[j], q8_operand(qrow, j), sn);
     else sn = mfma32(ka[j], qreg[j], sn);
 #pragma unroll
     for (int e = 0; e < EPQ; ++e) {
@@ -1163,6 +1181,122 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
   st.l += (q[0] + q[2]) + (q[1] + q[3]);
 }
 
+// Rows whose probabilities may go through the E4M3 PV product see at least
+// this many keys.  An E4M3 probability is off by up to 2^-4 of itself; with
+// hundreds of keys no single weight is large enough for that to move the
+// output by more than a few 1e-3 on standard-normal data, while a row with a
+// handful of keys could be moved by several 1e-2.
+constexpr int kMinKeysF8Pv = 256;
+
+// V^T operand of the E4M3 PV product for d-tile t of a 64-key tile (V rows
+// of the tile from vl, fp8, row-major at VPITCH): lane l takes column
+// 32 t + l % 32 and the 32 keys 32 (l / 32) + {0..7, 16..23, 8..15, 24..31}
+// of the tile -- the order in which the probabilities of one 32-key step
+// sit in a lane after pair_probs -- from four transposing reads (lane L of a
+// 16-lane group receives 8 consecutive keys of one column).
+template <int VPITCH>
+__device__ __forceinline__ i32x8 v_operand_f8pair(const uint8_t* vl, int t, int lane) {
+  const int L = lane & 15;
+  const int d0 = 32 * t + 16 * ((lane >> 4) & 1);
+  const uint8_t* src = vl + (32 * (lane >> 5) + (L >> 1)) * VPITCH + d0 + 8 * (L & 1);
+  const i32x2 a = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(src));
+  const i32x2 b = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(src + 16 * VPITCH));
+  const i32x2 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(src + 8 * VPITCH));
+  const i32x2 d = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(src + 24 * VPITCH));
+  return i32x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 16 probabilities (0 <= p <= 2^8) -> 16 E4M3 codes, byte i = code of p[i]
+// (round to nearest even; the range needs no saturation).
+__device__ __forceinline__ void pack_e4m3x16(const float* p, uint32_t (&w)[4]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * d], p[4 * d + 1], 0, false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(p[4 * d + 2], p[4 * d + 3], x, true);
+    w[d] = (uint32_t)x;
+  }
+}
+
+// The E4M3 probabilities of two consecutive 32-key steps (x: the earlier one,
+// y: the later one, each as this lane's 16 keys) rearranged for the B operand
+// of one 32x32x64 product: lanes < 32 end with all 32 keys of the earlier
+// step, lanes >= 32 with all 32 of the later one (one v_permlane32_swap per
+// dword: the upper half-wave of x trades places with the lower half of y).
+__device__ __forceinline__ i32x8 pair_probs(const uint32_t (&x)[4], const uint32_t (&y)[4]) {
+  i32x8 r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto s = __builtin_amdgcn_permlane32_swap((int)x[d], (int)y[d], false, false);
+    r[d] = (int)s[0];
+    r[4 + d] = (int)s[1];
+  }
+  return r;
+}
+
+// One pipelined 32-key step of the streamed schedule with fp8 queries whose
+// probabilities go through the E4M3 PV product: as stream_step, the score
+// product of the next step (K rows at kl) interleaved with the exp work of
+// this step (raw scores sc); then, by MODE:
+//   1  the first step of a 64-key tile: no PV product; the probabilities are
+//      kept in E4M3 (stash) with the running max they were taken against;
+//   2  the second step: its probabilities in E4M3 paired with the stash, one
+//      v_mfma_scale_f32_32x32x64_f8f6f4 per 32-wide d tile over the tile's 64
+//      V rows (from vl_tile).  The running max is an integer (log2 units), so
+//      the stash's rescale since it was taken, 2^(m_stash - m), is a power of
+//      two: the E8M0 block scale of its half of the keys (lanes < 32 supply
+//      the scale of k-block 0 of their column, lanes >= 32 of k-block 1).
+template <int D, int KPITCH, int VPITCH, int MODE>
+__device__ __forceinline__ void stream_step_f8(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
+                                               const uint8_t* kl, const uint8_t* vl_tile,
+                                               const uint8_t* qrow, float c,
+                                               uint32_t (&stash)[4], float& m_stash, int lane) {
+  static_assert(MODE == 1 || MODE == 2, "first or second step of a tile");
+  constexpr int NQ = D / 64;            // score MFMAs
+  constexpr int NT = D / 32;            // 32-wide d tiles of O
+  constexpr int EPQ = 16 / NQ;          // exps per score MFMA
+  const float nref = st.m == neg_inf() ? 0.f : -st.m;
+  float p[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sn[i] = 0.f;
+  i32x8 ka = k_operand_f8<KPITCH>(kl, 0, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    sn = mfma32_f8(ka, q8_operand(qrow, j), sn);
+    if (j + 1 < NQ) ka = k_operand_f8<KPITCH>(kl, 0, j + 1, lane);
+#pragma unroll
+    for (int e = 0; e < EPQ; ++e) {
+      const int i = j * EPQ + e;
+      p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, nref));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = p[i] + p[i + 8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] += q[i + 4];
+  st.l += (q[0] + q[2]) + (q[1] + q[3]);
+  if constexpr (MODE == 1) {
+    pack_e4m3x16(p, stash);
+    m_stash = st.m;
+  } else {
+    uint32_t cur[4];
+    pack_e4m3x16(p, cur);
+    const i32x8 pb = pair_probs(stash, cur);
+    int e = 127;
+    if (lane < 32) {
+      const float dm = m_stash - st.m;                 // an integer <= 0, or -inf/NaN when empty
+      e = dm > -127.f ? 127 + (int)dm : 0;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const i32x8 va = v_operand_f8pair<VPITCH>(vl_tile, t, lane);
+      st.o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, st.o[t], 0, 0, 0, 127, 0, e);
+    }
+  }
+}
+
 // Tiles are issued NB-2 ahead: at the top of tile t every wave has waited for
 // its loads of tiles t and t+1 and passed the barrier, so both are resident and
 // every wave is done with tile t-1, whose buffer then receives tile t+NB-1.
@@ -1174,7 +1308,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
                             const PageWalk& pw, int L, float c, float vdesc) {
   using Gm = Geo<D, FP8>;
   const SoftCap sc(p.softcap, c);
-  constexpr int NW = Block<MODE, D>::waves;
+  constexpr int NW = Block<MODE, D, QF8>::waves;
   constexpr int NB = Gm::ring_bufs;
   static_assert(NB >= 3 && NB <= 4, "ring of three or four tiles");
   using TL = TileLoads<D, FP8, NW>;
@@ -1185,13 +1319,19 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   const int last_tok = max(rm.ntok - 1, 0);
 
   // Q operands of this wave's rows, in registers (bf16, or E4M3 codes)
-  typename QOp<QF8>::reg qreg[QOp<QF8>::template n<D>::value];
+  typename QOp<QF8>::reg qreg[QOp<QF8>::template n<D>::value];   // bf16 queries only
+  // fp8 queries: the wave's E4M3 query rows live in LDS (registers go to the
+  // E4M3 PV product's state); this lane reads row lane % 32 from qrow
+  const uint8_t* qrow = nullptr;
   {
     const int r = r0 + (lane & 31);
     const bool ok = r < nrows;
     const int tok = ok ? r / rm.G : 0;
     const int h = rm.g * rm.G + (r - tok * rm.G);
     if constexpr (QF8) {
+      using LD = Lds<D, FP8, MODE>;
+      uint8_t* qw = smem + LD::q8_off + (wave * kCols + (lane & 31)) * LD::q8_pitch + 32 * (lane >> 5);
+      qrow = qw;
       // the loads are unconditional: a lane past the block's rows reads from
       // the first query row (head 0 of token 0 always exists), then drops it
       const int64_t off = ok ? (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D : 0;
@@ -1201,7 +1341,8 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
         u32x4 a = *reinterpret_cast<const u32x4*>(src + 64 * j);
         u32x4 b = *reinterpret_cast<const u32x4*>(src + 64 * j + 16);
         if (!ok) a = b = u32x4{0u, 0u, 0u, 0u};
-        qreg[j] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        *reinterpret_cast<u32x4*>(qw + 64 * j) = a;
+        *reinterpret_cast<u32x4*>(qw + 64 * j + 16) = b;
       }
     } else {
       const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
@@ -1262,21 +1403,62 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
                  wave);
       // steps 2t and 2t+1 read tiles t and t+1 (step -1 also reads tile 0)
       const int u_end = min(2 * t + 2, nsub);
-#pragma unroll 1
-      for (; u < u_end; ++u) {
-        const int tk = (u + 1) >> 1;                        // tile of step u+1's keys
-        const int tv = max(u, 0) >> 1;                      // tile of step u's keys
-        const uint8_t* kl = smem + (tk % NB) * Gm::tile_bytes + ((u + 1) & 1) * kSub * Gm::k_pitch;
-        const uint8_t* vl = smem + (tv % NB) * Gm::tile_bytes + Gm::tile_k_bytes + (u & 1) * kSub * Gm::v_pitch;
-        f32x16 sn[1];
-        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], kl, vl, qreg, c, lane);
+      // the scores of step u+1 (just computed into sn): cap, mask, row max
+      auto next_scores = [&](f32x16 (&sn)[1]) {
         if (u + 1 < nsub) {
           const int k1 = cb + (u + 1) * kSub;
           if (sc.on()) cap_tile(sn[0], sc);
           if (k1 + kSub > wave_kfull) mask_tile(sn[0], k1, klim, lane);
-          max_update<D, 1>(st, sn, c);
+          max_update<D, 1, QF8>(st, sn, c);
         }
         s_cur = sn[0];
+      };
+      auto k_rows = [&]() {                                  // K rows of step u+1's keys
+        const int tk = (u + 1) >> 1;
+        return smem + (tk % NB) * Gm::tile_bytes + ((u + 1) & 1) * kSub * Gm::k_pitch;
+      };
+      if constexpr (QF8) {
+        // Tile t visible to every row of the wave, and every row seeing at
+        // least kMinKeysF8Pv keys: its two steps' probabilities go through
+        // the E4M3 PV product together.  Steps of a masked (diagonal or
+        // tail) tile, and rows with few keys, keep the bf16 product.
+        if (wave_kfull >= kMinKeysF8Pv && cb + kTile * (t + 1) <= wave_kfull) {
+          if (u < 2 * t) {                                   // step -1 (t == 0): no keys of its own
+            f32x16 sn[1];
+            const uint8_t* vl = smem + Gm::tile_k_bytes + kSub * Gm::v_pitch;
+            stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, lane);
+            next_scores(sn);
+            ++u;
+          }
+          const uint8_t* vl_tile = smem + (t % NB) * Gm::tile_bytes + Gm::tile_k_bytes;
+          uint32_t stash[4];
+          float m_stash;
+          __builtin_amdgcn_sched_barrier(0);
+          {
+            f32x16 sn[1];
+            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 1>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, stash,
+                                                         m_stash, lane);
+            next_scores(sn);
+            ++u;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          {
+            f32x16 sn[1];
+            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 2>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, stash,
+                                                         m_stash, lane);
+            next_scores(sn);
+            ++u;
+          }
+          continue;
+        }
+      }
+#pragma unroll 1
+      for (; u < u_end; ++u) {
+        const int tv = max(u, 0) >> 1;                      // tile of step u's keys
+        const uint8_t* vl = smem + (tv % NB) * Gm::tile_bytes + Gm::tile_k_bytes + (u & 1) * kSub * Gm::v_pitch;
+        f32x16 sn[1];
+        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, lane);
+        next_scores(sn);
       }
     }
   }
@@ -1805,8 +1987,8 @@ __global__ __launch_bounds__(1024) void queue_setup_kernel(QueueSetupParams q) {
 // mixed batch (its own instance, so that its loop does not change the
 // register allocation of the one-item-per-workgroup kernel).
 template <int D, bool FP8, int MODE, bool QF8 = false, bool QUEUE = false>
-__global__ __launch_bounds__((Block<MODE, D>::threads))
-__attribute__((amdgpu_waves_per_eu(Block<MODE, D>::waves_per_eu, Block<MODE, D>::waves_per_eu)))
+__global__ __launch_bounds__((Block<MODE, D, QF8>::threads))
+__attribute__((amdgpu_waves_per_eu(Block<MODE, D, QF8>::waves_per_eu, Block<MODE, D, QF8>::waves_per_eu)))
 void attn_kernel(AttnParams p) {
   static_assert(!QF8 || (FP8 && MODE == kPrefill && Block<MODE, D>::stream), "fp8 queries: streamed fp8 prefill only");
   static_assert(!QUEUE || MODE == kMixed, "task queues: mixed batches only");
@@ -1870,7 +2052,7 @@ void attn_kernel(AttnParams p) {
     if (threadIdx.x == 0) meta[0] = 0;
     __syncthreads();
     int cnt = 0;
-    for (int j = threadIdx.x; j < p.num_seqs; j += Block<MODE, D>::threads) cnt += (p.cu_q_lens[j] / BQ + j <= x) ? 1 : 0;
+    for (int j = threadIdx.x; j < p.num_seqs; j += Block<MODE, D, QF8>::threads) cnt += (p.cu_q_lens[j] / BQ + j <= x) ? 1 : 0;
     if (cnt) atomicAdd(&meta[0], cnt);
     __syncthreads();
     b = meta[0] - 1;
@@ -2831,7 +3013,7 @@ template <int D, bool FP8, int MODE>
 hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if constexpr (FP8 && MODE == kPrefill && Block<MODE, D>::stream) {
     if (p.q_fp8) {
-      hipLaunchKernelGGL((attn_kernel<D, FP8, MODE, true>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
+      hipLaunchKernelGGL((attn_kernel<D, FP8, MODE, true>), grid, dim3(Block<MODE, D, true>::threads), 0, stream, p);
       return hipGetLastError();
     }
   }
@@ -2917,20 +3099,21 @@ int attention_lds_bytes(int head_dim, bool kv_fp8, Mode mode) {
 }
 
 template <int D>
-int block_rows_d(Mode mode) {
+int block_rows_d(Mode mode, bool q_fp8) {
   switch (mode) {
     case kDecode: return Block<kDecode, D>::waves * Block<kDecode, D>::nct * kCols;
-    case kPrefill: return Block<kPrefill, D>::waves * Block<kPrefill, D>::nct * kCols;
+    case kPrefill:
+      return q_fp8 ? Block<kPrefill, D, true>::waves * kCols : Block<kPrefill, D>::waves * Block<kPrefill, D>::nct * kCols;
     case kMixed: return Block<kMixed, D>::waves * Block<kMixed, D>::nct * kCols;
   }
   return 0;
 }
 
-int block_rows(int head_dim, Mode mode) {
+int block_rows(int head_dim, Mode mode, bool q_fp8) {
   switch (head_dim) {
-    case 64: return block_rows_d<64>(mode);
-    case 128: return block_rows_d<128>(mode);
-    case 256: return block_rows_d<256>(mode);
+    case 64: return block_rows_d<64>(mode, q_fp8);
+    case 128: return block_rows_d<128>(mode, q_fp8);
+    case 256: return block_rows_d<256>(mode, q_fp8);
   }
   return 0;
 }
