@@ -59,12 +59,16 @@ struct AttnParams {
                                 // the task queues in sched (queue_sched_ints ints)
 };
 
-// Task queues of a mixed launch, in the workspace (int32 words): two draw
-// counters (prefill-type and decode-type items), kQueueSlots arrival counters
-// (one per compute unit id), then the item offsets of each sequence in the
+// Task queues of a mixed launch, in the workspace (int32 words): kQueueCtrs
+// draw counters (one per XCD share of the prefill-type list, then the
+// decode-type list's, then a spare), kQueueSlots arrival counters (one per
+// compute unit id), then the item offsets of each sequence in the
 // prefill-type list [B+1] and in the decode-type list [B+1].
+constexpr int kQueueShares = 8;                   // XCDs of an MI355X
+constexpr int kQueueDecodeCtr = kQueueShares;
+constexpr int kQueueCtrs = kQueueShares + 2;
 constexpr int kQueueSlots = 1024;
-inline int64_t queue_sched_ints(int64_t num_seqs) { return 2 + kQueueSlots + 2 * (num_seqs + 1); }
+inline int64_t queue_sched_ints(int64_t num_seqs) { return kQueueCtrs + kQueueSlots + 2 * (num_seqs + 1); }
 
 struct QueueSetupParams {
   const int32_t* cu_q_lens;     // [B+1]

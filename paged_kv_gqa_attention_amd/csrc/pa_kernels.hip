@@ -1848,41 +1848,66 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
 
 // Task-queue schedule of a mixed batch.  Work items are split into two lists
 // by the kind of work: prefill-type items (sequence b with q_len_b * G > 32:
-// one per (q-block, KV head), each sequence's q-blocks last-first, i.e. most
-// keys first) are compute-bound, decode-type items (one per (sequence, KV
-// head)) are memory-bound.  queue_setup_kernel lays both lists out (per
-// sequence offsets) and zeroes the counters.  The grid holds the workgroups
-// that fit on the device at once; each one draws items from the two lists
-// with an atomic counter per list until both are empty.  The first workgroup
-// to arrive on a compute unit prefers the prefill list and the second the
-// decode list, so that a compute-bound and a memory-bound item tend to share
-// each compute unit; a workgroup whose preferred list is empty takes the
-// other.  Every draw either claims one of the finitely many items or finds
-// both lists empty, so every workgroup ends without waiting on another.
+// one per (q-block, KV head); within a sequence KV-head major, each head's
+// q-blocks last-first, i.e. most keys first) are compute-bound, decode-type
+// items (one per (sequence, KV head)) are memory-bound.  queue_setup_kernel
+// lays both lists out (per sequence offsets) and zeroes the counters.  The
+// grid holds the workgroups that fit on the device at once; each one draws
+// items from the two lists with atomic counters until both are empty.  The
+// first workgroup to arrive on a compute unit prefers the prefill list and
+// the second the decode list, so that a compute-bound and a memory-bound item
+// tend to share each compute unit; a workgroup whose preferred list is empty
+// takes the other.  The prefill list is cut into kQueueShares contiguous
+// shares with a counter each: a workgroup draws from the share of its own
+// XCD (workgroups are dealt to the XCDs round-robin by linear id) and only
+// when that is empty from the next ones, so the q-blocks of one (sequence,
+// KV head), which read the same K/V rows, run under one L2.  Every draw
+// either claims one of the finitely many items or finds all lists empty, so
+// every workgroup ends without waiting on another.
 constexpr int kQmPref = 8;      // LDS metadata words used by the queue loop
 constexpr int kQmWhich = 9;
 constexpr int kQmItem = 10;
 constexpr int kQmSeq = 11;
 
+// Claim a prefill-type item: the own share first, then the others in turn;
+// -1 when every share is empty.
+__device__ __forceinline__ int draw_prefill(int32_t* ctr, int n, int xcd) {
+  for (int s = 0; s < kQueueShares; ++s) {
+    const int y = (xcd + s) % kQueueShares;
+    const int lo = (int)((int64_t)y * n / kQueueShares);
+    const int hi = (int)((int64_t)(y + 1) * n / kQueueShares);
+    if (lo >= hi) continue;
+    const int k = atomicAdd(&ctr[y], 1);
+    if (lo + k < hi) return lo + k;
+  }
+  return -1;
+}
+
 template <int D, bool FP8, int MODE>
 __device__ void queue_mixed(const AttnParams& p, uint8_t* smem, int32_t* pcache, int* meta) {
   constexpr int NTH = Block<MODE, D>::threads;
   const int B = p.num_seqs;
-  if (threadIdx.x == 0) meta[kQmPref] = atomicAdd(&p.sched[2 + (__smid() & (kQueueSlots - 1))], 1) & 1;
+  const int xcd = blockIdx.x % kQueueShares;
+  if (threadIdx.x == 0)
+    meta[kQmPref] = atomicAdd(&p.sched[kQueueCtrs + (__smid() & (kQueueSlots - 1))], 1) & 1;
   __syncthreads();
   int pref = meta[kQmPref];
   for (;;) {
     __syncthreads();                            // the previous item is done with LDS and meta
     if (threadIdx.x == 0) {
-      // list l's offsets start at sched + 2 + kQueueSlots + l (B + 1); its
-      // item count is the last offset
-      const int32_t* lists = p.sched + 2 + kQueueSlots;
-      int which = pref;
-      int k = atomicAdd(&p.sched[which], 1);
-      if (k >= lists[which * (B + 1) + B]) {
-        which ^= 1;
-        k = atomicAdd(&p.sched[which], 1);
-        if (k >= lists[which * (B + 1) + B]) k = -1;
+      // list l's offsets start at sched + kQueueCtrs + kQueueSlots + l (B + 1);
+      // its item count is the last offset
+      const int32_t* lists = p.sched + kQueueCtrs + kQueueSlots;
+      const int np = lists[B], nd = lists[(B + 1) + B];
+      int which = pref, k = -1;
+      for (int attempt = 0; attempt < 2 && k < 0; ++attempt, which ^= 1) {
+        if (which == 0) {
+          k = draw_prefill(p.sched, np, xcd);
+        } else {
+          k = atomicAdd(&p.sched[kQueueDecodeCtr], 1);
+          if (k >= nd) k = -1;
+        }
+        if (k >= 0) break;
       }
       meta[kQmWhich] = which;
       meta[kQmItem] = k;
@@ -1894,7 +1919,7 @@ __device__ void queue_mixed(const AttnParams& p, uint8_t* smem, int32_t* pcache,
     if (k < 0) break;
     pref = which;
     // the sequence whose range [off[b], off[b+1]) holds item k
-    const int32_t* off = p.sched + 2 + kQueueSlots + which * (B + 1);
+    const int32_t* off = p.sched + kQueueCtrs + kQueueSlots + which * (B + 1);
     for (int j = threadIdx.x; j < B; j += NTH)
       if (off[j] <= k && k < off[j + 1]) meta[kQmSeq] = j;
     __syncthreads();
@@ -1907,8 +1932,8 @@ __device__ void queue_mixed(const AttnParams& p, uint8_t* smem, int32_t* pcache,
     int g, i0, ntok;
     if (which == 0) {
       const int nb = (q_len + BQ - 1) / BQ;
-      g = r % p.num_kv_heads;
-      i0 = (nb - 1 - r / p.num_kv_heads) * BQ;
+      g = r / nb;
+      i0 = (nb - 1 - (r - g * nb)) * BQ;
       ntok = min(BQ, q_len - i0);
     } else {
       g = r;
@@ -1963,7 +1988,7 @@ __global__ __launch_bounds__(1024) void queue_setup_kernel(QueueSetupParams q) {
     sd[t] += d;
     __syncthreads();
   }
-  int32_t* offp = q.sched + 2 + kQueueSlots;
+  int32_t* offp = q.sched + kQueueCtrs + kQueueSlots;
   int32_t* offd = offp + B + 1;
   int ep = sp[t] - cp, ed = sd[t] - cd;
   for (int j = j0; j < j1; ++j) {
@@ -1978,8 +2003,8 @@ __global__ __launch_bounds__(1024) void queue_setup_kernel(QueueSetupParams q) {
     offp[B] = sp[1023];
     offd[B] = sd[1023];
   }
-  if (t < 2) q.sched[t] = 0;
-  for (int i = t; i < kQueueSlots; i += 1024) q.sched[2 + i] = 0;
+  if (t < kQueueCtrs) q.sched[t] = 0;
+  for (int i = t; i < kQueueSlots; i += 1024) q.sched[kQueueCtrs + i] = 0;
 }
 
 // QF8: queries arrive as E4M3 codes (fp8 inputs); only the streamed prefill

@@ -136,7 +136,7 @@ def test_split_heuristic_and_workspace():
     p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048))
     info = B.pa_plan_get_info(p)
     assert info.num_splits == 1 and info.balanced_workgroups == 0 and info.queue_workgroups == 512
-    assert B.pa_workspace_bytes(p) == ((2 + 1024 + 2 * 257) * 4 + 255) // 256 * 256
+    assert B.pa_workspace_bytes(p) == ((10 + 1024 + 2 * 257) * 4 + 255) // 256 * 256
     B.pa_plan_destroy(p)
     # balanced decode on request; below -1 is invalid
     p = B.pa_plan(desc(num_seqs=256, page_table_cols=128, max_total_q=256, max_seq_len=2048,
@@ -146,14 +146,15 @@ def test_split_heuristic_and_workspace():
     assert B.pa_workspace_bytes(p) >= 2 * 512 * 4 * (128 + 1) * 4
     # -1 also puts mixed runs on the task queues: one workgroup per resident
     # slot of the mixed kernel (two per CU at D 128 bf16); the workspace holds
-    # 2 counters, 1024 arrival counters and two offset lists of B + 1
+    # 10 counters (8 prefill-list shares, decode list, spare), 1024 arrival
+    # counters and two offset lists of B + 1
     assert info.queue_workgroups == 2 * 256
-    assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 257) * 4
+    assert B.pa_workspace_bytes(p) >= (10 + 1024 + 2 * 257) * 4
     B.pa_plan_destroy(p)
     assert plan_status(num_splits=-2) == B.PA_ERR_INVALID
     p = B.pa_plan(desc(num_seqs=4096, page_table_cols=16, max_total_q=4096, num_splits=-1))
     assert B.pa_plan_get_info(p).queue_workgroups == 512
-    assert B.pa_workspace_bytes(p) >= (2 + 1024 + 2 * 4097) * 4
+    assert B.pa_workspace_bytes(p) >= (10 + 1024 + 2 * 4097) * 4
     B.pa_plan_destroy(p)
     p = B.pa_plan(desc(num_splits=1))
     assert B.pa_plan_get_info(p).queue_workgroups == 0

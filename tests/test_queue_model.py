@@ -1,9 +1,12 @@
 """Host model of the task-queue schedule of mixed batches (the setup
-kernel's per-sequence item lists and the main kernel's item -> (sequence,
-q-block, KV head) mapping), checked over random batches: every q-block of
-every KV head is claimed exactly once, the prefill-type list holds exactly
-the sequences with q_len * G > 32, and each sequence's q-blocks come
-most-keys-first.  Mirrors queue_setup_kernel and queue_mixed; no GPU."""
+kernel's per-sequence item lists, the XCD shares of the prefill-type list
+and the main kernel's item -> (sequence, q-block, KV head) mapping), checked
+over random batches: every q-block of every KV head is claimed exactly once
+whatever order the workgroups of the eight XCDs draw in, the prefill-type
+list holds exactly the sequences with q_len * G > 32, each (sequence, KV
+head)'s q-blocks come most-keys-first and, except where a share boundary
+cuts it, inside one XCD share.  Mirrors queue_setup_kernel, draw_prefill and
+queue_mixed; no GPU."""
 import numpy as np
 import pytest
 
@@ -50,8 +53,8 @@ def claim(which, ks, off, q_lens, Hkv, BQ):
     ql = q_lens[b]
     if which == 0:
         nb = (ql + BQ - 1) // BQ
-        g = r % Hkv
-        i0 = (nb - 1 - r // Hkv) * BQ
+        g = r // nb
+        i0 = (nb - 1 - (r - g * nb)) * BQ
         ntok = np.minimum(BQ, ql - i0)
     else:
         g, i0, ntok = r, np.zeros_like(r), ql
@@ -95,3 +98,65 @@ def test_queue_lists_cover_every_item_once(seed):
             for g in range(Hkv):
                 want[(b, 0, g)] = 1
     assert seen == want
+
+
+SHARES = 8
+
+
+def share_bounds(n):
+    return [(y * n // SHARES, (y + 1) * n // SHARES) for y in range(SHARES)]
+
+
+def draw_prefill(ctr, n, xcd):
+    """draw_prefill of the kernel: the own share first, then the others."""
+    for s in range(SHARES):
+        y = (xcd + s) % SHARES
+        lo, hi = y * n // SHARES, (y + 1) * n // SHARES
+        if lo >= hi:
+            continue
+        k = ctr[y]
+        ctr[y] += 1
+        if lo + k < hi:
+            return lo + k
+    return -1
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_xcd_shares_claim_every_prefill_item_once(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.choice([0, 1, 5, 7, 8, 9, 100, 2048, 2051]))
+    ctr = [0] * SHARES
+    got = []
+    # workgroups of random XCDs draw until every list is empty; an empty
+    # draw ends that workgroup, as in the kernel
+    alive = list(range(512))
+    while alive:
+        w = alive[int(rng.integers(0, len(alive)))]
+        k = draw_prefill(ctr, n, w % SHARES)
+        if k < 0:
+            alive.remove(w)
+        else:
+            got.append(k)
+    assert sorted(got) == list(range(n))
+    assert sum(hi - lo for lo, hi in share_bounds(n)) == n
+
+
+def test_mixed_24b_pairs_stay_in_one_share():
+    # the serving mix: 8 prefill chunks of 1000 tokens (q-blocks of 32 at
+    # G = 4) and 248 decode rows; each (sequence, KV head)'s 32 q-blocks are
+    # contiguous in the prefill list, so a share boundary cuts at most one
+    # pair per share
+    q_lens = np.array([1000] * 8 + [1] * 248, np.int64)
+    Hkv, BQ = 8, 32
+    offp, _ = setup_lists(q_lens, 4, Hkv, BQ)
+    n = int(offp[-1])
+    ks = np.arange(n, dtype=np.int64)
+    b, g, i0, _ = claim(0, ks, offp, q_lens, Hkv, BQ)
+    share = np.zeros(n, np.int64)
+    for y, (lo, hi) in enumerate(share_bounds(n)):
+        share[lo:hi] = y
+    pairs = {}
+    for bb, gg, yy in zip(b.tolist(), g.tolist(), share.tolist()):
+        pairs.setdefault((bb, gg), set()).add(yy)
+    assert len(pairs) == 64
+    assert sum(len(v) > 1 for v in pairs.values()) <= SHARES - 1
