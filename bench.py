@@ -59,18 +59,34 @@ def kernel_sha() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this workload, or None when absent or taken on a different kernel source."""
-    path = os.path.join(PROFILE_DIR, "%s_counters.md" % workload)
+def read_profile(workload: str, kind: str, key: str):
+    """A figure (`key: value`) from the committed rocprofv3 summary
+    profiles/<workload>_<kind>.md, or None when absent or taken on a different
+    kernel source."""
+    path = os.path.join(PROFILE_DIR, "%s_%s.md" % (workload, kind))
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel_sha:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_bytes or m_sha.group(1) != kernel_sha():
+    m_val = re.search(r"%s:\s*([0-9.eE+-]+)" % re.escape(key), text)
+    if not m_sha or not m_val or m_sha.group(1) != kernel_sha():
         return None
-    return float(m_bytes.group(1))
+    return float(m_val.group(1))
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel (FETCH_SIZE + WRITE_SIZE,
+    copy-calibrated), or None."""
+    return read_profile(workload, "counters", "hbm_bytes_per_launch")
+
+
+def read_counters(workload: str):
+    """Measured HBM traffic and SQ figures of the workload's dominant kernel
+    from the committed summaries (None where absent or stale)."""
+    return {"traffic": read_traffic(workload),
+            "mfma_busy_pct": read_profile(workload, "sq_counters", "mfma_busy_pct"),
+            "lds_bank_conflicts_per_access": read_profile(workload, "sq_counters",
+                                                          "lds_bank_conflicts_per_access")}
 
 
 def validate(w, out, lse, rows, oracle_rows):
@@ -425,6 +441,18 @@ def main():
             print("# %s validated=%s ms=%.4f frac=%.3f" % (r["workload"], r["valid"], r["ms_per_step"],
                                                            r["roofline_frac"]),
                   file=sys.stderr, flush=True)
+    for name, e in sec.items():
+        # the measured figures of each line's dominant kernel, beside its roofline
+        if e["bound"] == "mfma" or (name.startswith(("mixed", "mla")) and
+                                    e["tflops"] / BF16_PEAK_TFLOPS > e["alg_gbs"] / HBM_PEAK_GBS):
+            peak = e.get("peak_tflops", BF16_PEAK_TFLOPS)
+            roof = {"bound": "mfma", "achieved": round(e["tflops"], 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(e["tflops"] / peak, 4)}
+        else:
+            roof = {"bound": "hbm", "achieved": round(e["alg_gbs"], 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(e["alg_gbs"] / HBM_PEAK_GBS, 4)}
+        roof.update(read_counters(name))
+        e["roofline"] = roof
     w = prim["w"]
     alg_bytes = prim["kv_bytes"] + prim["qo_bytes"]
     achieved = alg_bytes / (prim["ms_per_step"] * 1e-3) / 1e9
@@ -452,6 +480,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic("decode_llama8b"),
+                     "mfma_busy_pct": read_profile("decode_llama8b", "sq_counters", "mfma_busy_pct"),
                      "kernel": "attn_kernel<128, bf16, decode>",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,

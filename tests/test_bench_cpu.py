@@ -44,3 +44,16 @@ def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_sha() == h
     src.write_text("int f() { return 2; }\n")
     assert bench.kernel_sha() != h
+
+
+def test_sq_figures_need_the_current_kernel_hash(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILE_DIR", str(tmp_path))
+    assert bench.read_counters("w") == {"traffic": None, "mfma_busy_pct": None,
+                                        "lds_bank_conflicts_per_access": None}
+    (tmp_path / "w_sq_counters.md").write_text(
+        "kernel_sha: %s\nmfma_busy_pct: 39.80\nlds_bank_conflicts_per_access: 0.4760\n" % bench.kernel_sha())
+    c = bench.read_counters("w")
+    assert c["mfma_busy_pct"] == 39.8 and c["lds_bank_conflicts_per_access"] == 0.476
+    assert c["traffic"] is None
+    (tmp_path / "w_sq_counters.md").write_text("kernel_sha: 0000000000000000\nmfma_busy_pct: 39.80\n")
+    assert bench.read_counters("w")["mfma_busy_pct"] is None
