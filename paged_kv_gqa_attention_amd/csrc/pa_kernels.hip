@@ -556,6 +556,34 @@ __device__ __forceinline__ void probs(SoftmaxState<D>& st, const f32x16 (&s)[NS]
   st.l += psum;
 }
 
+// max_update for one tile of the streamed schedule, with the slack test done
+// per lane first: each lane compares the max of its own 16 raw scores with
+// thr = (m + slack) / c; only when some lane of the wave exceeds it is the row
+// max taken over both lanes of the row and the accumulator rescaled.  The
+// common case is then eight v_max3 and one compare.  thr and nref (the
+// exponent offset of the probabilities, -m or 0 while m is -inf) follow st.m.
+template <int D, bool INT_M>
+__device__ __forceinline__ void max_update_lane(SoftmaxState<D>& st, const f32x16& s, float c, float& thr,
+                                                float& nref) {
+  float mx = neg_inf();
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[i]), s[i + 1]);
+  if (__builtin_amdgcn_ballot_w64(mx > thr)) {
+    mx = fmaxf(mx, xor32(mx));
+    const float mxs = mx * c;
+    const float m_new = INT_M ? __builtin_ceilf(fmaxf(st.m, mxs)) : fmaxf(st.m, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[t][i] *= alpha;
+    st.m = m_new;
+    thr = (m_new + kRescaleSlack) / c;
+    nref = m_new == neg_inf() ? 0.f : -m_new;
+  }
+}
+
 template <int D, int NS>
 __device__ __forceinline__ void softmax_p(SoftmaxState<D>& st, const f32x16 (&s)[NS], float c,
                                           bf16x8 (&pb)[NS][2]) {
@@ -1124,12 +1152,11 @@ template <int D, bool FP8, int KPITCH, int VPITCH, bool QF8>
 __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
                                             const uint8_t* kl, const uint8_t* vl,
                                             const typename QOp<QF8>::reg (&qreg)[QOp<QF8>::template n<D>::value],
-                                            const uint8_t* qrow, float c, int lane) {
+                                            const uint8_t* qrow, float c, float nref, int lane) {
   constexpr int NQ = QOp<QF8>::template n<D>::value;   // score MFMAs (k-steps over the head dim)
   constexpr int NT = D / 32;            // 32-wide d tiles of O
   constexpr int NV = 2 * NT;            // PV MFMAs; operand v = (tile v % NT, half v / NT)
   constexpr int EPQ = 16 / NQ;          // exps per score MFMA
-  const float nref = st.m == neg_inf() ? 0.f : -st.m;
   typename QOp<QF8>::reg ka[NQ];
   bf16x8 va[NV];
   float p[16];
@@ -1248,13 +1275,12 @@ __device__ __forceinline__ i32x8 pair_probs(const uint32_t (&x)[4], const uint32
 template <int D, int KPITCH, int VPITCH, int MODE>
 __device__ __forceinline__ void stream_step_f8(SoftmaxState<D>& st, const f32x16& sc, f32x16& sn,
                                                const uint8_t* kl, const uint8_t* vl_tile,
-                                               const uint8_t* qrow, float c,
+                                               const uint8_t* qrow, float c, float nref,
                                                uint32_t (&stash)[4], float& m_stash, int lane) {
   static_assert(MODE == 1 || MODE == 2, "first or second step of a tile");
   constexpr int NQ = D / 64;            // score MFMAs
   constexpr int NT = D / 32;            // 32-wide d tiles of O
   constexpr int EPQ = 16 / NQ;          // exps per score MFMA
-  const float nref = st.m == neg_inf() ? 0.f : -st.m;
   float p[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) sn[i] = 0.f;
@@ -1364,6 +1390,8 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
 
   SoftmaxState<D> st;
   state_init(st);
+  float thr = neg_inf();                  // (st.m + slack) / c, raw-score units
+  float nref = 0.f;                       // -st.m, or 0 while st.m is -inf
   TL tl;
   tl.init(wave, lane);
   PageWalk w = pw;
@@ -1409,7 +1437,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
           const int k1 = cb + (u + 1) * kSub;
           if (sc.on()) cap_tile(sn[0], sc);
           if (k1 + kSub > wave_kfull) mask_tile(sn[0], k1, klim, lane);
-          max_update<D, 1, QF8>(st, sn, c);
+          max_update_lane<D, QF8>(st, sn[0], c, thr, nref);
         }
         s_cur = sn[0];
       };
@@ -1426,7 +1454,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
           if (u < 2 * t) {                                   // step -1 (t == 0): no keys of its own
             f32x16 sn[1];
             const uint8_t* vl = smem + Gm::tile_k_bytes + kSub * Gm::v_pitch;
-            stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, lane);
+            stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, nref, lane);
             next_scores(sn);
             ++u;
           }
@@ -1436,7 +1464,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
           __builtin_amdgcn_sched_barrier(0);
           {
             f32x16 sn[1];
-            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 1>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, stash,
+            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 1>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, nref, stash,
                                                          m_stash, lane);
             next_scores(sn);
             ++u;
@@ -1444,7 +1472,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
           __builtin_amdgcn_sched_barrier(0);
           {
             f32x16 sn[1];
-            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 2>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, stash,
+            stream_step_f8<D, Gm::k_pitch, Gm::v_pitch, 2>(st, s_cur, sn[0], k_rows(), vl_tile, qrow, c, nref, stash,
                                                          m_stash, lane);
             next_scores(sn);
             ++u;
@@ -1457,7 +1485,7 @@ __device__ void stream_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
         const int tv = max(u, 0) >> 1;                      // tile of step u's keys
         const uint8_t* vl = smem + (tv % NB) * Gm::tile_bytes + Gm::tile_k_bytes + (u & 1) * kSub * Gm::v_pitch;
         f32x16 sn[1];
-        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, lane);
+        stream_step<D, FP8, Gm::k_pitch, Gm::v_pitch, QF8>(st, s_cur, sn[0], k_rows(), vl, qreg, qrow, c, nref, lane);
         next_scores(sn);
       }
     }
