@@ -353,7 +353,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     modes = {"decode_llama8b": "decode", "prefill_causal": "prefill",
-             "mixed_24b": "mixed", "decode_fp8_long": "decode"}
+             "prefill_causal_d256": "prefill", "mixed_24b": "mixed", "decode_fp8_long": "decode"}
 
     def strip(r):
         return {k: v for k, v in r.items() if k != "w"}
@@ -388,12 +388,12 @@ def main():
         file=sys.stderr, flush=True)
     sec = {}
     if not a.no_secondary:
-        for name in ("prefill_causal", "mixed_24b", "decode_fp8_long"):
-            # the prefill's CPU check covers 8 tokens x 8 heads of every sequence
-            rp = (8, 8) if name == "prefill_causal" else (2, 2)
+        for name in ("prefill_causal", "mixed_24b", "decode_fp8_long", "prefill_causal_d256"):
+            # the prefills' CPU check covers 8 tokens x 8 heads of every sequence
+            rp = (8, 8) if name.startswith("prefill") else (2, 2)
             r = bench_workload(name, modes[name], max(5, a.steps // 2), a.warmup, cpu_leg,
                                sample_rows_per_seq=rp[0], heads=rp[1])
-            bound = "mfma" if name == "prefill_causal" else "hbm"
+            bound = "mfma" if name.startswith("prefill") else "hbm"
             if bound == "mfma":
                 frac = r["tflops"] / BF16_PEAK_TFLOPS
             elif name == "mixed_24b":

@@ -149,9 +149,10 @@ struct Geo {
   // transposed read touches across banks.
   static constexpr int v_pitch = row_bytes + 32;
   // decode schedule: each wave step stages dec_step keys (K rows, then V rows,
-  // in one region).  fp8 at head dim 256 runs one wave per SIMD and has the
-  // registers to keep two 32-key tiles (32 KB) in flight per wave.
-  static constexpr int dec_tiles = (D == 256 && FP8) ? 2 : 1;
+  // in one region): one 32-key tile per step at every geometry (two tiles at
+  // fp8 head dim 256 held 32 KB per wave in registers and spilled in the
+  // mixed kernels; pure decode of that geometry runs the ring schedule).
+  static constexpr int dec_tiles = 1;
   static constexpr int dec_step = kSub * dec_tiles;
   static constexpr int dec_keys_per_lane = (dec_step * chunks) / kWave;   // >= 1
   static constexpr int stage_bytes = CMax<dec_step * k_pitch, dec_step * v_pitch>::value;
@@ -267,6 +268,17 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
 // Value of lane l^32.  v_permlane32_swap exchanges the upper half of its first
 // operand with the lower half of its second; with both operands x, lanes < 32
 // find their partner in the second result and lanes >= 32 in the first.
+// threadIdx.x through an opaque move.  The schedules of one work item call
+// this instead of reading threadIdx.x: in the task-queue kernel, which runs
+// many items per workgroup, the per-lane addresses derived from it are then
+// recomputed for each item instead of being hoisted to the kernel prologue
+// and kept live (spilled) across the whole item loop.
+__device__ __forceinline__ int item_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
 __device__ __forceinline__ float xor32(float x) {
   const int xi = __builtin_bit_cast(int, x);
   const auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
@@ -300,7 +312,7 @@ __device__ __forceinline__ void fill_pcache(PageWalk& w, int32_t* pcache, int k_
   w.first_page = k_begin >> w.shift;
   w.pcache = pcache;
   const int n = last_key >= k_begin ? (last_key >> w.shift) - w.first_page + 1 : 0;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) pcache[i] = w.pt_row[w.first_page + i];
+  for (int i = item_tid(); i < n; i += blockDim.x) pcache[i] = w.pt_row[w.first_page + i];
 }
 
 // NK consecutive keys from key0 (a multiple of NK), one 16-byte chunk each,
@@ -628,6 +640,7 @@ template <int D, int DS = D>
 __device__ void write_rows(const AttnParams& p, const SoftmaxState<DS>& st, float l_tot, int r0,
                            const RowMap& rm, int slot, float vdesc, int lane, int col0 = 0,
                            bool lse_owner = true) {
+  lane = item_tid() & (kWave - 1);       // re-derived here: nothing per-lane stays live for the epilogue
   const int r = r0 + (lane & 31);
   const int tok = r / rm.G;
   if (tok >= rm.ntok) return;
@@ -683,8 +696,8 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   constexpr int NWB = Block<MODE, D>::waves;             // waves in the workgroup
   constexpr int NW = Gm::template DecWaves<NWB>::value;   // waves that stage K/V
   constexpr int NK = Gm::dec_keys_per_lane;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = item_tid() & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(item_tid() >> 6);
   const int nrows = rm.ntok * rm.G;
 
   // key window [klo, khi), clipped by the causal limit of the last token
@@ -710,7 +723,7 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     u32x4 qv[QPT];
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-      const int u = threadIdx.x + k * NTH;
+      const int u = item_tid() + k * NTH;
       const int r = u / cpr, ch = u % cpr;
       qv[k] = u32x4{0u, 0u, 0u, 0u};
       if (u < kCols * cpr && r < nrows) {
@@ -723,7 +736,7 @@ __device__ void keysplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
     fill_pcache(w, pcache, klo, min(khi, klo + chunk_keys));
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
-      const int u = threadIdx.x + k * NTH;
+      const int u = item_tid() + k * NTH;
       if (u < kCols * cpr) *reinterpret_cast<u32x4*>(ql + (u / cpr) * Gm::q_pitch + (u % cpr) * 16) = qv[k];
     }
   }
@@ -857,8 +870,8 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
   constexpr int NUNITS = (kTile * Gm::chunks) / NK;
   constexpr int NCT = Block<MODE, D>::nct;               // 32-row column tiles per wave
   constexpr int NS = kTile / kSub;                       // score tiles per LDS tile
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = item_tid() & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(item_tid() >> 6);
   const int nrows = rm.ntok * rm.G;
   const int r0 = wave * kCols * NCT;                     // this wave's first packed row
   const int last_tok = max(rm.ntok - 1, 0);
@@ -905,7 +918,7 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) state_init(st[ct]);
 
-  const int unit = threadIdx.x;
+  const int unit = item_tid();
   const bool loader = unit < NUNITS;
   const int chunk = unit % Gm::chunks;
   const int kg = unit / Gm::chunks;
@@ -937,11 +950,13 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
           const int k0 = key0 + kSub * n;
-          // all K operands of the tile first, so the score MFMAs do not wait
-          // on LDS one by one
+          // K operands of the tile: all of them first (head dim <= 128), so the
+          // score MFMAs do not wait on LDS one by one; at head dim 256 eight
+          // ahead of their MFMAs, which keeps the operands out of scratch
+          constexpr int KA = D <= 128 ? D / 16 : 8;
           bf16x8 ka[D / 16];
 #pragma unroll
-          for (int j = 0; j < D / 16; ++j) ka[j] = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j, lane);
+          for (int j = 0; j < KA; ++j) ka[j] = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j, lane);
           // two independent accumulation chains (even / odd k-steps) halve the
           // dependent-MFMA latency of the score product
           f32x16 s[NCT][1], s2[NCT];
@@ -950,21 +965,26 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[ct][0][i] = s2[ct][i] = 0.f;
 #pragma unroll
-          for (int j = 0; j < D / 16; j += 2)
+          for (int j = 0; j < D / 16; j += 2) {
+            if (KA < D / 16 && j + KA < D / 16) {
+              ka[j + KA] = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j + KA, lane);
+              ka[j + KA + 1] = k_operand<D, FP8, Gm::k_pitch>(kl, kSub * n, j + KA + 1, lane);
+            }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
               s[ct][0] = mfma32(ka[j], qreg[ct][j], s[ct][0]);
               s2[ct] = mfma32(ka[j + 1], qreg[ct][j + 1], s2[ct]);
             }
+          }
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) s[ct][0] += s2[ct];
-          // V operands requested before the softmax: their LDS latency hides
-          // under the exp work
+          // V operands requested before the softmax, so that their LDS latency
+          // hides under the exp work: all of them (head dim <= 128), or the
+          // first eight, the rest eight ahead of their MFMAs
+          constexpr int VA = D <= 128 ? D / 16 : 8;
           bf16x8 va[D / 32][2];
 #pragma unroll
-          for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) va[t][h] = v_operand<FP8, Gm::v_pitch>(vl, kSub * n, t, h, lane);
+          for (int v = 0; v < VA; ++v) va[v >> 1][v & 1] = v_operand<FP8, Gm::v_pitch>(vl, kSub * n, v >> 1, v & 1, lane);
           if (sc.on()) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) cap_tile(s[ct][0], sc);
@@ -977,11 +997,12 @@ __device__ void rowsplit_item(const AttnParams& p, uint8_t* smem, int32_t* pcach
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) softmax_p<D, 1>(st[ct], s[ct], c, pb[ct]);
 #pragma unroll
-          for (int t = 0; t < D / 32; ++t)
+          for (int v = 0; v < D / 16; ++v) {
+            if (VA < D / 16 && v + VA < D / 16)
+              va[(v + VA) >> 1][(v + VA) & 1] = v_operand<FP8, Gm::v_pitch>(vl, kSub * n, (v + VA) >> 1, (v + VA) & 1, lane);
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) st[ct].o[t] = mfma32(va[t][h], pb[ct][0][h], st[ct].o[t]);
+            for (int ct = 0; ct < NCT; ++ct) st[ct].o[v >> 1] = mfma32(va[v >> 1][v & 1], pb[ct][0][v & 1], st[ct].o[v >> 1]);
+          }
         }
       }
       if (loader) {

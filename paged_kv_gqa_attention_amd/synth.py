@@ -289,6 +289,15 @@ def prefill_causal(seed: int = 3, **kw) -> Workload:
                  num_kv_heads=8, head_dim=128, page_size=64, seed=seed, pt_cols=64, **kw)
 
 
+def prefill_causal_d256(seed: int = 8, **kw) -> Workload:
+    """16 causal prefills, q_len = L ~ U[512, 4096], Hq/Hkv 16/4, D 256, page 64:
+    the context head dim 256 of the supported scope, at the flops of
+    prefill_causal (half the heads, twice the head dim)."""
+    L = uniform_int(512, 4096, 16, seed, 0)
+    return build(name="prefill_causal_d256", seq_lens=L, q_lens=L, num_q_heads=16,
+                 num_kv_heads=4, head_dim=256, page_size=64, seed=seed, pt_cols=64, **kw)
+
+
 def mixed_24b(seed: int = 4, shuffle: bool = False, **kw) -> Workload:
     """8 prefill chunks of 1000 new tokens on 0..1000 cached tokens, then 248
     decode rows with L ~ U[1000, 2000]; Hq/Hkv 32/8, D 128, page 16."""
@@ -420,6 +429,7 @@ WORKLOADS = {
     "tiny_mixed": tiny_mixed,
     "decode_llama8b": decode_llama8b,
     "prefill_causal": prefill_causal,
+    "prefill_causal_d256": prefill_causal_d256,
     "mixed_24b": mixed_24b,
     "decode_fp8_long": decode_fp8_long,
     "mla_decode_h16": mla_decode_h16,

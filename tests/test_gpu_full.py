@@ -1,4 +1,4 @@
-"""GPU parity at full size: the four large workloads in the launch configuration
+"""GPU parity at full size: the large workloads in the launch configuration
 bench.py times (plus the other entry points that accept them), compared with
 the oracle element by element.  The decode workloads are checked on every
 row; the prefill and the serving mix on rows that touch every work item of
@@ -59,6 +59,15 @@ def test_prefill_causal_full():
     run_sampled(w, "mixed", per_seq=6)
 
 
+def test_prefill_causal_d256_full():
+    # head dim 256 (row-split schedule), every (q-block, wave slice, KV head)
+    w = synth.prefill_causal_d256()
+    pa = PagedAttention(w)
+    rows = H.cover_rows(w, pa.info.q_block_tokens)
+    run_rows(w, "prefill", rows)
+    run_sampled(w, "mixed", per_seq=4)
+
+
 def test_mixed_24b_full():
     w = synth.mixed_24b()
     pa = PagedAttention(w)
@@ -79,7 +88,8 @@ def test_decode_fp8_long_full():
 def test_full_size_outputs_are_finite_everywhere():
     # every row, not just the sample: poisoned tails never leak
     for make, mode in ((synth.decode_llama8b, "decode"), (synth.decode_fp8_long, "decode"),
-                       (synth.mixed_24b, "mixed"), (synth.prefill_causal, "prefill")):
+                       (synth.mixed_24b, "mixed"), (synth.prefill_causal, "prefill"),
+                       (synth.prefill_causal_d256, "prefill")):
         w = make()
         x = DeviceInputs(w)
         pa = PagedAttention(w)
