@@ -2975,22 +2975,47 @@ constexpr int kAppendTokens = 16;     // new tokens per workgroup, at most
 __host__ __device__ inline int append_tokens_per_block(bool fp8) { return fp8 ? 4 : kAppendTokens; }
 constexpr int kAppendBatch = 4;       // 16-byte groups a thread loads before it stores
 
+// Division by a per-tensor descale d: q = x / d, correctly rounded.  For d in
+// [2^-60, 2^60] (a wave-uniform test) the quotient of an x clamped to
+// +-449 d comes from the exact reciprocal y = 1/d and one FMA correction:
+// q0 = x y, r = x - q0 d (exact, one FMA), q = q0 + r y.  With y the
+// correctly rounded reciprocal and no underflow in r this is the correctly
+// rounded quotient (the FMA-based division correction of Markstein); a
+// host check over every bf16 value against thousands of descales of that
+// range finds every quotient of magnitude 2^-10 .. 448 equal to IEEE
+// division and every E4M3 code equal.  Smaller quotients encode to zero either way (their
+// sign is kept from q0), larger ones saturate, and the clamp keeps q0 finite.
+// Outside that range of d the kernel divides.
+struct DescaleDiv {
+  float d, y, m;
+  bool fast;
+  __device__ explicit DescaleDiv(float d_) : d(d_), y(1.f / d_), m(449.f * d_),
+                                            fast(d_ >= 0x1p-60f && d_ <= 0x1p60f) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    if (!fast) return x / d;
+    const float xc = __builtin_amdgcn_fmed3f(x, -m, m);
+    const float q0 = xc * y;
+    const float r = __builtin_fmaf(-q0, d, xc);
+    return __builtin_copysignf(__builtin_fmaf(r, y, q0), q0);
+  }
+};
+
 // 8 bf16 values (one 16-byte group) -> 8 OCP E4M3 codes of the binary32
-// quotients value / d.  Each quotient is correctly rounded (IEEE division);
-// finite ones are clamped to +-448 (saturation, infinities included) and the
-// hardware conversion rounds to nearest even.  The conversion gives every NaN
-// the code 0xFF, so NaN codes are rewritten as 0x7F with the quotient's sign
-// (a branch no lane takes unless its group holds a NaN).
-__device__ __forceinline__ u32x2 e4m3_encode8(u32x4 v, float d) {
+// quotients value / d (correctly rounded, DescaleDiv); finite ones are
+// clamped to +-448 (saturation, infinities included) and the hardware
+// conversion rounds to nearest even.  The conversion gives every NaN the
+// code 0xFF, so NaN codes are rewritten as 0x7F with the value's sign (a
+// branch no lane takes unless its group holds a NaN).
+__device__ __forceinline__ u32x2 e4m3_encode8(u32x4 v, const DescaleDiv& div) {
   float q[8];
   bool any_nan = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t h = (v[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-    const float x = __builtin_bit_cast(float, h << 16) / d;
-    const bool nan = (__builtin_bit_cast(uint32_t, x) & 0x7FFFFFFFu) > 0x7F800000u;
+    const float x = __builtin_bit_cast(float, h << 16);
+    const bool nan = (h & 0x7FFFu) > 0x7F80u;
     any_nan |= nan;
-    q[i] = nan ? x : __builtin_amdgcn_fmed3f(x, 448.0f, -448.0f);
+    q[i] = nan ? x : __builtin_amdgcn_fmed3f(div(x), 448.0f, -448.0f);
   }
   u32x2 out;
 #pragma unroll
@@ -3052,8 +3077,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int per_kv = p.num_kv_heads * (p.head_dim / 8);      // 16-byte groups per K (or V) row
   const int per_token = 2 * per_kv;
   const int groups = min(tpb, total - t0) * per_token;
-  const float kd = p.fp8 ? *p.k_descale : 1.f;
-  const float vd = p.fp8 ? *p.v_descale : 1.f;
+  const DescaleDiv kd(p.fp8 ? *p.k_descale : 1.f);
+  const DescaleDiv vd(p.fp8 ? *p.v_descale : 1.f);
   for (int base = threadIdx.x; base < groups; base += kAppendBatch * 256) {
     u32x4 v[kAppendBatch];
     int64_t dst[kAppendBatch];
