@@ -285,6 +285,16 @@ __device__ __forceinline__ float xor32(float x) {
   return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
 }
 
+// Value of lane l^16 (v_permlane16_swap exchanges the odd 16-lane rows of its
+// first operand with the even rows of its second; with both operands x, lanes
+// in even rows find their partner in the second result, the others in the
+// first).
+__device__ __forceinline__ float xor16(float x) {
+  const int xi = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // K / V staging: a "unit" is NK consecutive keys x one 16-byte chunk of their rows
 // ---------------------------------------------------------------------------
@@ -2183,25 +2193,27 @@ constexpr int kMlaDk = 576;
 struct MlaGeo {
   static constexpr int row_bytes = kMlaDk * 2;
   static constexpr int chunks = row_bytes / 16;
-  static constexpr int pitch = row_bytes + 16;
+  static constexpr int pitch = row_bytes + 32;
   static constexpr int slots = pitch / 16;
   static constexpr int loads = (kSub * slots + 63) / 64;
   static constexpr int tile_bytes = loads * 1024;
-  static constexpr int per_wave = (loads + kDecWaves - 1) / kDecWaves;
-  static constexpr int min_per_wave = loads / kDecWaves;
 };
 
 // Direct global->LDS loads of one 32-key tile: load i writes slots
 // [64 i, 64 i + 64) of the tile; lane l fetches the 16 bytes that belong at
 // slot 64 i + l (a pad slot, or a slot past the 32 rows, re-fetches chunk 0 of
-// row 31: in bounds, never read).  Wave w issues loads w, w + 4, ...
+// row 31: in bounds, never read).  Loader wave w of NW issues loads w,
+// w + NW, ...
+template <int NW>
 struct MlaLoads {
-  uint32_t slot_rc[MlaGeo::per_wave];   // row in the tile (high half), byte offset in the row
+  static constexpr int per_wave = (MlaGeo::loads + NW - 1) / NW;
+  static constexpr int min_per_wave = MlaGeo::loads / NW;
+  uint32_t slot_rc[per_wave];   // row in the tile (high half), byte offset in the row
 
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < MlaGeo::per_wave; ++j) {
-      const int slot = 64 * (wave + j * kDecWaves) + lane;
+    for (int j = 0; j < per_wave; ++j) {
+      const int slot = 64 * (wave + j * NW) + lane;
       int row = slot / MlaGeo::slots;
       int ch = slot - row * MlaGeo::slots;
       if (row >= kSub) {
@@ -2222,23 +2234,23 @@ struct MlaLoads {
       const uint8_t* base = pool + (int64_t)w.pcache[(key0 >> w.shift) - w.first_page] * w.page_bytes +
                             (uint32_t)(key0 & slot_mask) * (uint32_t)MlaGeo::row_bytes;
 #pragma unroll
-      for (int j = 0; j < MlaGeo::per_wave; ++j) {
-        const int i = wave + j * kDecWaves;
+      for (int j = 0; j < per_wave; ++j) {
+        const int i = wave + j * NW;
         if (i < MlaGeo::loads)
           dma_load_16(base + ((slot_rc[j] >> 16) * (uint32_t)MlaGeo::row_bytes + (slot_rc[j] & 0xFFFFu)),
                       buf + 1024 * i);
       }
       return;
     }
-    int key[MlaGeo::per_wave], page[MlaGeo::per_wave];
+    int key[per_wave], page[per_wave];
 #pragma unroll
-    for (int j = 0; j < MlaGeo::per_wave; ++j) {
+    for (int j = 0; j < per_wave; ++j) {
       key[j] = min(key0 + (int)(slot_rc[j] >> 16), w.kend - 1);
       page[j] = w.pcache[(key[j] >> w.shift) - w.first_page];
     }
 #pragma unroll
-    for (int j = 0; j < MlaGeo::per_wave; ++j) {
-      const int i = wave + j * kDecWaves;
+    for (int j = 0; j < per_wave; ++j) {
+      const int i = wave + j * NW;
       if (i < MlaGeo::loads) {
         const uint8_t* src = pool + (int64_t)page[j] * w.page_bytes +
                              ((uint32_t)(key[j] & slot_mask) * (uint32_t)MlaGeo::row_bytes + (slot_rc[j] & 0xFFFFu));
@@ -2292,7 +2304,7 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
   w.row_stride_b = MlaGeo::row_bytes;
   w.shift = p.page_shift;
   w.klimit = L;
-  MlaLoads ml;
+  MlaLoads<kDecWaves> ml;
   ml.init(wave, lane);
   const int chunk_keys = kPcacheEntries << w.shift;
   for (int cb = klo; cb < khi; cb += chunk_keys) {
@@ -2309,7 +2321,7 @@ __device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int
     for (int t = 0; t < ntiles; ++t) {
       // tile t must have landed; up to R-2 later tiles may stay in flight
       if (R >= 3 && t + 1 < ntiles)
-        wait_vmem<(R >= 3 ? MlaGeo::min_per_wave : 0)>();
+        wait_vmem<(R >= 3 ? MlaLoads<kDecWaves>::min_per_wave : 0)>();
       else
         wait_vmem<0>();
       ring_barrier();
@@ -2584,65 +2596,93 @@ __device__ __forceinline__ f32x4 mfma16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 constexpr int kMlaHeads = 16;                    // query heads per wave
 constexpr int kMlaQSteps = kMlaDk / 32;          // 32-wide k-steps of the score product
-constexpr int kMlaVTiles = kMlaLatent / 16;      // 16-wide value tiles of O
+constexpr int kMlaVTilesHalf = kMlaLatent / 32;  // 16-wide value tiles in half the columns
 
-// Running state of one wave: its 16 heads over its keys.  Lane l holds head
-// l % 16; o[t][i] is output column 16 t + 4 (l / 16) + i; l is this lane's
-// part of the row sum (its four keys of each block); m is the same on the
-// four lanes of a head.
+// Waves of a head-split MLA workgroup: eight, two per SIMD (waves w and
+// w + 4 share 16 heads and split each tile's keys for the scores and the
+// value columns for the output), so that one wave's LDS reads and softmax
+// overlap the other's MFMAs; with four, each wave takes all 512 columns of its
+// heads and runs alone on its SIMD.
+constexpr int kMlaHsWaves = 8;
+
+// Running state of one wave: its 16 heads over its keys and NVT 16-wide value
+// tiles.  Lane l holds head l % 16; o[t][i] is value column
+// col0 + 16 t + 4 (l / 16) + i; l is this lane's part of the row sum (its
+// eight keys of each tile); m is the same on the four lanes of a head.
+template <int NVT>
 struct MlaState {
-  f32x4 o[kMlaVTiles];
+  f32x4 o[NVT];
   float m, l;
 };
 
-// One 16-key block (rows kr .. kr + 15 of the LDS tile at kl; keys key0 ..
-// key0 + 15, of which those >= khi are masked): scores S^T = K Q^T on
-// 16x16x32 MFMAs (lane l: head l % 16, keys 4 (l / 16) .. +3), the online
-// softmax, and O^T += V^T P^T on 16x16x16 MFMAs, P straight from the score
-// registers (the B operand layout of the 16x16x16 product is the accumulator
-// layout of the score product).  V^T operands come from transposing LDS
-// reads: 16-lane group g reads keys 4 g .. 4 g + 3 of 16 columns and lane L
-// receives column L's four keys.
-template <bool CAP>
-__device__ __forceinline__ void mla_block(MlaState& st, const uint8_t* kl, int kr, int key0, int khi,
-                                          const bf16x8 (&qreg)[kMlaQSteps], float c, const SoftCap& sc,
-                                          int lane) {
-  // One wave per SIMD: every LDS operand read is issued one step ahead of
-  // the MFMAs that consume it (scheduling barriers keep that order), so its
-  // latency hides behind the previous step's products.
-  constexpr int NP = kMlaQSteps / 2;            // pairs of score k-steps
+__device__ __forceinline__ bf16x8 join_bf16x4(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One 32-key tile (LDS at kl; keys k0 .. k0 + 31, of which those >= khi are
+// masked) for this wave's 16 heads: scores S^T = K Q^T of both 16-key halves
+// on 16x16x32 MFMAs (lane l: head l % 16, keys 4 (l / 16) .. +3 of each
+// half), the online softmax over the eight keys a lane holds, and
+// O^T += V^T P^T for NVT value tiles from column col0 on 16x16x32 MFMAs with
+// the 32 keys as the contraction.  The contraction order is a permutation
+// of the keys: index 8 g + i is key 4 g + i for i < 4 and key 16 + 4 g + i - 4
+// otherwise, which is the order in which lane group g already holds its
+// probabilities (the B operand, straight from the score registers) and the
+// order two transposing LDS reads give the A operand (16-lane group g reads
+// keys 4 g .. 4 g + 3 of 16 columns from each half; lane L receives column
+// L's keys).
+template <bool CAP, int NVT>
+__device__ __forceinline__ void mla_tile(MlaState<NVT>& st, const uint8_t* kl, int k0, int khi,
+                                         const bf16x8 (&qreg)[kMlaQSteps], float c, const SoftCap& sc,
+                                         int col0, int lane) {
+  // every LDS operand read is issued one step ahead of the MFMAs that consume
+  // it (scheduling barriers keep that order)
+  constexpr int NP = kMlaQSteps / 2;            // pairs of score k-steps per half
+  constexpr int NI = 2 * NP;                    // score steps of the tile
   constexpr int VG = 4;                         // value tiles per step
-  const uint8_t* krow = kl + (kr + (lane & 15)) * MlaGeo::pitch + 16 * (lane >> 4);
+  constexpr int half = 16 * MlaGeo::pitch;      // LDS offset of keys 16 .. 31
+  const uint8_t* krow = kl + (lane & 15) * MlaGeo::pitch + 16 * (lane >> 4);
   const int L = lane & 15;
-  const uint8_t* vsrc = kl + (kr + 4 * (lane >> 4) + (L >> 2)) * MlaGeo::pitch + 8 * (L & 3);
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  u32x4 ka[NP][2];
+  const uint8_t* vsrc = kl + (4 * (lane >> 4) + (L >> 2)) * MlaGeo::pitch + 8 * (L & 3) + 2 * col0;
+  f32x4 s[2][2];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 ka[NI][2];
   ka[0][0] = *reinterpret_cast<const u32x4*>(krow);
   ka[0][1] = *reinterpret_cast<const u32x4*>(krow + 64);
 #pragma unroll
-  for (int jp = 0; jp < NP; ++jp) {
-    if (jp + 1 < NP) {
-      ka[jp + 1][0] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1));
-      ka[jp + 1][1] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1) + 64);
+  for (int it = 0; it < NI; ++it) {
+    if (it + 1 < NI) {
+      const uint8_t* a = krow + ((it + 1) / NP) * half + 128 * ((it + 1) % NP);
+      ka[it + 1][0] = *reinterpret_cast<const u32x4*>(a);
+      ka[it + 1][1] = *reinterpret_cast<const u32x4*>(a + 64);
     }
-    s0 = mfma16_k32(as_bf16x8(ka[jp][0]), qreg[2 * jp], s0);
-    s1 = mfma16_k32(as_bf16x8(ka[jp][1]), qreg[2 * jp + 1], s1);
+    const int hb = it / NP, jp = it % NP;
+    s[hb][0] = mfma16_k32(as_bf16x8(ka[it][0]), qreg[2 * jp], s[hb][0]);
+    s[hb][1] = mfma16_k32(as_bf16x8(ka[it][1]), qreg[2 * jp + 1], s[hb][1]);
     __builtin_amdgcn_sched_barrier(0);
   }
   // the first value operands load while the softmax runs
-  i16x4 va[kMlaVTiles / VG][VG];
+  i16x4 va[NVT / VG][VG][2];
 #pragma unroll
-  for (int u = 0; u < VG; ++u) va[0][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * u));
-  __builtin_amdgcn_sched_barrier(0);
-  const int kb = key0 + 4 * (lane >> 4);
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float x = s0[i] + s1[i];
-    if constexpr (CAP) x = cap1(x, sc);
-    v[i] = kb + i < khi ? x : neg_inf();
+  for (int u = 0; u < VG; ++u) {
+    va[0][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * u));
+    va[0][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + half + 32 * u));
   }
-  float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  __builtin_amdgcn_sched_barrier(0);
+  const int kb = k0 + 4 * (lane >> 4);
+  float v[8];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = s[hb][0][i] + s[hb][1][i];
+      if constexpr (CAP) x = cap1(x, sc);
+      v[4 * hb + i] = kb + 16 * hb + i < khi ? x : neg_inf();
+    }
+  float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, xor32(mx));
   const float mxs = mx * c;
@@ -2654,27 +2694,29 @@ __device__ __forceinline__ void mla_block(MlaState& st, const uint8_t* kl, int k
     const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
     st.l *= alpha;
 #pragma unroll
-    for (int t = 0; t < kMlaVTiles; ++t) st.o[t] *= alpha;
+    for (int t = 0; t < NVT; ++t) st.o[t] *= alpha;
     st.m = m_new;
   }
   const float nref = st.m == neg_inf() ? 0.f : -st.m;
-  float pr[4];
+  float pr[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], c, nref));
-  st.l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const u32x2 pw{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
-  const bf16x4 pb = __builtin_bit_cast(bf16x4, pw);
+  for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], c, nref));
+  st.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  const bf16x8 pb = pack_bf16x8(pr);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int g = 0; g < kMlaVTiles / VG; ++g) {
-    if (g + 1 < kMlaVTiles / VG) {
+  for (int g = 0; g < NVT / VG; ++g) {
+    if (g + 1 < NVT / VG) {
 #pragma unroll
-      for (int u = 0; u < VG; ++u)
-        va[g + 1][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * (VG * (g + 1) + u)));
+      for (int u = 0; u < VG; ++u) {
+        const uint8_t* a = vsrc + 32 * (VG * (g + 1) + u);
+        va[g + 1][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+        va[g + 1][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + half));
+      }
     }
 #pragma unroll
     for (int u = 0; u < VG; ++u)
-      st.o[VG * g + u] = mfma16_k16(__builtin_bit_cast(bf16x4, va[g][u]), pb, st.o[VG * g + u]);
+      st.o[VG * g + u] = mfma16_k32(join_bf16x4(va[g][u][0], va[g][u][1]), pb, st.o[VG * g + u]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -2682,12 +2724,13 @@ __device__ __forceinline__ void mla_block(MlaState& st, const uint8_t* kl, int k
 // The key loop of a head-split MLA item: 32-key tiles of latent rows stream
 // through a ring of four LDS buffers by direct loads (issued three tiles
 // ahead, so that about 110 KB per compute unit are in flight; one barrier per
-// tile); every wave runs both 16-key blocks of each tile for its heads.
-template <bool CAP>
+// tile; the NW waves share each tile's loads).
+template <bool CAP, int NW, int NVT>
 __device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
                                          int klo, int khi, const bf16x8 (&qreg)[kMlaQSteps], float c,
-                                         const SoftCap& sc, MlaState& st, int wave, int lane) {
+                                         const SoftCap& sc, MlaState<NVT>& st, int col0, int wave, int lane) {
   constexpr int R = MlaHsLds::ring;
+  using Loads = MlaLoads<NW>;
   PageWalk w;
   w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
   w.page_bytes = p.kv_page_bytes;
@@ -2695,7 +2738,7 @@ __device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, 
   w.row_stride_b = MlaGeo::row_bytes;
   w.shift = p.page_shift;
   w.klimit = L;
-  MlaLoads ml;
+  Loads ml;
   ml.init(wave, lane);
   const int chunk_keys = kPcacheEntries << w.shift;
   for (int cb = klo; cb < khi; cb += chunk_keys) {
@@ -2716,9 +2759,9 @@ __device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, 
       // min_per_wave loads of this wave)
       const int ahead = min(R - 2, ntiles - 1 - t);
       if (ahead >= 2)
-        wait_vmem<2 * MlaGeo::min_per_wave>();
+        wait_vmem<2 * Loads::min_per_wave>();
       else if (ahead == 1)
-        wait_vmem<MlaGeo::min_per_wave>();
+        wait_vmem<Loads::min_per_wave>();
       else
         wait_vmem<0>();
       ring_barrier();
@@ -2726,25 +2769,213 @@ __device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, 
       // iteration, which every wave has left (barrier above)
       if (t + R - 1 < ntiles)
         ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
-      const uint8_t* kl = smem + (t % R) * MlaGeo::tile_bytes;
-      const int k0 = cb + t * kSub;
+      mla_tile<CAP, NVT>(st, smem + (t % R) * MlaGeo::tile_bytes, cb + t * kSub, khi, qreg, c, sc, col0, lane);
+    }
+  }
+}
+
+// LDS of a key-pair MLA workgroup: a ring of four 32-key tiles, the score
+// exchange buffer (one 1 KB record per wave), then a page-id cache of 512
+// entries (half the usual, so that all of it fits in 160 KB).
+struct MlaPairLds {
+  static constexpr int ring = 4;
+  static constexpr int pcache_entries = 512;
+  static constexpr int xbuf_off = ring * MlaGeo::tile_bytes;
+  static constexpr int pcache_off = xbuf_off + kMlaHsWaves * kWave * 16 + 64;
+  static constexpr int bytes = pcache_off + pcache_entries * 4;
+  static_assert(bytes <= kLdsMax, "MLA LDS budget exceeded");
+};
+
+// Scores S^T = K Q^T of one 16-key half of a tile (rows 16 kh .. 16 kh + 15
+// of the LDS tile at kl) for this wave's 16 heads, on 16x16x32 MFMAs: lane l
+// gets head l % 16, keys 4 (l / 16) .. +3 of the half.  Operand reads run one
+// k-step pair ahead of their MFMAs.
+__device__ __forceinline__ f32x4 mla_half_scores(const uint8_t* kl, int kh, const bf16x8 (&qreg)[kMlaQSteps],
+                                                 int lane) {
+  constexpr int NP = kMlaQSteps / 2;
+  const uint8_t* krow = kl + (16 * kh + (lane & 15)) * MlaGeo::pitch + 16 * (lane >> 4);
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  u32x4 ka[NP][2];
+  ka[0][0] = *reinterpret_cast<const u32x4*>(krow);
+  ka[0][1] = *reinterpret_cast<const u32x4*>(krow + 64);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int key0 = k0 + 16 * hb;
-        if (key0 < ce) mla_block<CAP>(st, kl, 16 * hb, key0, khi, qreg, c, sc, lane);
+  for (int jp = 0; jp < NP; ++jp) {
+    if (jp + 1 < NP) {
+      ka[jp + 1][0] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1));
+      ka[jp + 1][1] = *reinterpret_cast<const u32x4*>(krow + 128 * (jp + 1) + 64);
+    }
+    s0 = mfma16_k32(as_bf16x8(ka[jp][0]), qreg[2 * jp], s0);
+    s1 = mfma16_k32(as_bf16x8(ka[jp][1]), qreg[2 * jp + 1], s1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return s0 + s1;
+}
+
+// The softmax of one 32-key tile (keys k0 .. k0 + 31, those >= khi masked)
+// from the scores of both halves (h0: keys 0 .. 15, h1: keys 16 .. 31, in
+// the score layout), then O^T += V^T P^T over NVT value tiles from column
+// col0, on 16x16x32 MFMAs with the tile's 32 keys as the contraction (key
+// order as in mla_tile).  Every wave of a pair runs the same operations on
+// the same values, so their running states stay equal.
+template <bool CAP, int NVT>
+__device__ __forceinline__ void mla_tile_pv(MlaState<NVT>& st, const uint8_t* kl, int k0, int khi, f32x4 h0,
+                                            f32x4 h1, float c, const SoftCap& sc, int col0, int lane) {
+  constexpr int VG = 4;                         // value tiles per step
+  constexpr int half = 16 * MlaGeo::pitch;
+  const int L = lane & 15;
+  const uint8_t* vsrc = kl + (4 * (lane >> 4) + (L >> 2)) * MlaGeo::pitch + 8 * (L & 3) + 2 * col0;
+  i16x4 va[NVT / VG][VG][2];
+#pragma unroll
+  for (int u = 0; u < VG; ++u) {
+    va[0][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * u));
+    va[0][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + half + 32 * u));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const int kb = k0 + 4 * (lane >> 4);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x0 = h0[i], x1 = h1[i];
+    if constexpr (CAP) {
+      x0 = cap1(x0, sc);
+      x1 = cap1(x1, sc);
+    }
+    v[i] = kb + i < khi ? x0 : neg_inf();
+    v[4 + i] = kb + 16 + i < khi ? x1 : neg_inf();
+  }
+  float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  mx = fmaxf(mx, xor16(mx));
+  mx = fmaxf(mx, xor32(mx));
+  const float mxs = mx * c;
+  if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
+    __asm__ volatile("" ::: "memory");
+    const float m_new = fmaxf(st.m, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) st.o[t] *= alpha;
+    st.m = m_new;
+  }
+  const float nref = st.m == neg_inf() ? 0.f : -st.m;
+  float pr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], c, nref));
+  st.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+  const bf16x8 pb = pack_bf16x8(pr);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < NVT / VG; ++g) {
+    if (g + 1 < NVT / VG) {
+#pragma unroll
+      for (int u = 0; u < VG; ++u) {
+        const uint8_t* a = vsrc + 32 * (VG * (g + 1) + u);
+        va[g + 1][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+        va[g + 1][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + half));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VG; ++u)
+      st.o[VG * g + u] = mfma16_k32(join_bf16x4(va[g][u][0], va[g][u][1]), pb, st.o[VG * g + u]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The key loop of a key-pair MLA item (eight waves, two per SIMD): waves w
+// and w + 4 own the same 16 heads; wave w scores keys 0 .. 15 of every tile
+// and wave w + 4 keys 16 .. 31, and they swap those scores through LDS, so no
+// product is computed twice; then both run the same softmax over the 32 keys
+// and each accumulates its half of the 512 value columns.  Software
+// pipelined: after barrier A of step t, tile t + 1 has landed (tile t + 2 may
+// still be in flight) and every wave's scores of tile t are in the exchange
+// buffer; the key-half-1 waves issue the loads of tile t + 3 (into the
+// buffer of tile t - 1, which every wave has left); each wave reads its
+// partner's scores, runs the softmax and value product of tile t and scores
+// its half of tile t + 1; barrier B (every partner read done) precedes the
+// write of those scores.
+template <bool CAP>
+__device__ __forceinline__ void mla_pair_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
+                                              int klo, int khi, const bf16x8 (&qreg)[kMlaQSteps], float c,
+                                              const SoftCap& sc, MlaState<kMlaVTilesHalf>& st, int kh, int col0,
+                                              int wave, int lane) {
+  constexpr int R = MlaPairLds::ring;
+  static_assert(R == 4, "the waits below keep at most one more tile in flight");
+  using Loads = MlaLoads<kMlaHsWaves / 2>;
+  uint8_t* xbuf = smem + MlaPairLds::xbuf_off;
+  const int xmine = (wave * kWave + lane) * 16;
+  const int xpart = ((wave ^ 4) * kWave + lane) * 16;
+  PageWalk w;
+  w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
+  w.page_bytes = p.kv_page_bytes;
+  w.head_off = 0;
+  w.row_stride_b = MlaGeo::row_bytes;
+  w.shift = p.page_shift;
+  w.klimit = L;
+  Loads ml;
+  ml.init(wave & 3, lane);
+  const bool loader = kh == 1;
+  const int chunk_keys = MlaPairLds::pcache_entries << w.shift;
+  for (int cb = klo; cb < khi; cb += chunk_keys) {
+    const int ce = min(khi, cb + chunk_keys);
+    __syncthreads();
+    fill_pcache(w, pcache, cb, ce);
+    wait_vmem_all();                            // Q loads and page-table reads
+    __syncthreads();
+    const int ntiles = (ce - cb + kSub - 1) / kSub;
+    if (loader) {
+#pragma unroll
+      for (int t = 0; t < R - 1; ++t)
+        if (t < ntiles) ml.issue(p.k_pool, w, cb + t * kSub, smem + t * MlaGeo::tile_bytes, wave & 3);
+    }
+    // tile 0 (tiles 1 and 2 may stay in flight)
+    if (ntiles > 2)
+      wait_vmem<2 * Loads::min_per_wave>();
+    else if (ntiles > 1)
+      wait_vmem<Loads::min_per_wave>();
+    else
+      wait_vmem<0>();
+    ring_barrier();
+    f32x4 mine = mla_half_scores(smem, kh, qreg, lane);
+    *reinterpret_cast<f32x4*>(xbuf + xmine) = mine;
+#pragma unroll 1
+    for (int t = 0; t < ntiles; ++t) {
+      if (t + 2 < ntiles)                       // tile t + 1 (tile t + 2 may stay in flight)
+        wait_vmem<Loads::min_per_wave>();
+      else
+        wait_vmem<0>();
+      ring_barrier();                           // A
+      // the loads of tile t + 3 (into the buffer of tile t - 1, which every
+      // wave has left), by the key-half-1 waves only: while they wait on the
+      // load path, their partners on the same SIMDs run ahead
+      const bool more = t + R - 1 < ntiles;
+      if (loader && more)
+        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave & 3);
+      const f32x4 part = *reinterpret_cast<const f32x4*>(xbuf + xpart);
+      mla_tile_pv<CAP, kMlaVTilesHalf>(st, smem + (t % R) * MlaGeo::tile_bytes, cb + t * kSub, khi,
+                                       kh == 0 ? mine : part, kh == 0 ? part : mine, c, sc, col0, lane);
+      if (t + 1 < ntiles) {
+        mine = mla_half_scores(smem + ((t + 1) % R) * MlaGeo::tile_bytes, kh, qreg, lane);
+        ring_barrier();                         // B
+        *reinterpret_cast<f32x4*>(xbuf + xmine) = mine;
       }
     }
   }
 }
 
 // One head-split MLA item: the keys [klo, khi) of sequence b for head group
-// hg (p.group heads starting at hg * p.group; wave w takes heads
-// 16 w .. 16 w + 15 of it), then its outputs -- final rows (slot < 0), a
-// split-KV partial record (split schedule) or a balanced partial record in
-// slot `slot`.
+// hg (p.group heads starting at hg * p.group), then its outputs -- final rows
+// (slot < 0), a split-KV partial record (split schedule) or a balanced
+// partial record in slot `slot`.  Wave w takes heads 16 (w % 4) .. +15 of the
+// group and value columns [col0, col0 + 16 NVT) with col0 = 16 NVT (w / 4):
+// with eight waves, waves w and w + 4 compute the same scores and softmax
+// and each accumulates half of the 512 columns.
+template <int NW>
 __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int hg, int L, int klo,
                             int khi, int slot, int wave, int lane) {
-  const int hl = wave * kMlaHeads + (lane & 15);  // head within the group
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int NVT = NW == 8 ? kMlaVTilesHalf : kMlaLatent / 16;
+  const int hl = (wave & 3) * kMlaHeads + (lane & 15);  // head within the group
+  const int kh = wave >> 2;                              // key half (eight waves)
+  const int col0 = 16 * NVT * kh;
   const int h = hg * p.group + hl;
   const bool hok = hl < p.group && h < p.num_q_heads;
   // the B operand of k-step j: head hl's query values 32 j + 8 (lane / 16) .. +7
@@ -2760,16 +2991,23 @@ __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   float c, vdesc;
   score_scales<false>(p, c, vdesc);
   const SoftCap sc(p.softcap, c);
-  MlaState st;
+  MlaState<NVT> st;
 #pragma unroll
-  for (int t = 0; t < kMlaVTiles; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NVT; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = neg_inf();
   st.l = 0.f;
   if (khi > klo) {
-    if (sc.on())
-      mla_hs_keys<true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
-    else
-      mla_hs_keys<false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
+    if constexpr (NW == 8) {
+      if (sc.on())
+        mla_pair_keys<true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
+      else
+        mla_pair_keys<false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
+    } else {
+      if (sc.on())
+        mla_hs_keys<true, NW, NVT>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, col0, wave, lane);
+      else
+        mla_hs_keys<false, NW, NVT>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, col0, wave, lane);
+    }
   }
   // the row sum: this lane's keys, then the head's four lanes
   st.l += __shfl_xor(st.l, 16);
@@ -2778,48 +3016,59 @@ __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   const bool empty = !(st.l > 0.f);
   const float inv = empty ? 0.f : vdesc / st.l;
   const float lse2 = empty ? neg_inf() : st.m + __builtin_amdgcn_logf(st.l);
-  const int d_lane = 4 * (lane >> 4);
+  const int d_lane = col0 + 4 * (lane >> 4);
+  const bool lse_lane = lane < 16 && col0 == 0;
   if (slot >= 0) {
     // balanced records hold the group's rows (p.group of them) per slot
     const int64_t row = p.balanced ? (int64_t)slot * p.group + hl
                                    : ((int64_t)slot * p.max_total_q + b) * p.num_q_heads + h;
-    if (lane < 16) p.part_lse[row] = lse2;
+    if (lse_lane) p.part_lse[row] = lse2;
     if (empty) return;
     float* dst = p.part_o + row * kMlaLatent + d_lane;
 #pragma unroll
-    for (int t = 0; t < kMlaVTiles; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = st.o[t] * inv;
+    for (int t = 0; t < NVT; ++t) *reinterpret_cast<f32x4*>(dst + 16 * t) = st.o[t] * inv;
   } else {
     uint16_t* dst = p.out + (int64_t)b * p.o_stride_t + (int64_t)h * kMlaLatent + d_lane;
 #pragma unroll
-    for (int t = 0; t < kMlaVTiles; ++t)
+    for (int t = 0; t < NVT; ++t)
       *reinterpret_cast<u32x2*>(dst + 16 * t) =
           u32x2{pack_bf16x2(st.o[t][0] * inv, st.o[t][1] * inv), pack_bf16x2(st.o[t][2] * inv, st.o[t][3] * inv)};
-    if (p.lse && lane < 16) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
+    if (p.lse && lse_lane) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
   }
 }
+
+template <int NW>
+struct MlaHsLayout {
+  using type = MlaHsLds;
+};
+template <>
+struct MlaHsLayout<8> {
+  using type = MlaPairLds;
+};
 
 // Head-split MLA decode, for head groups of 33 to 64 heads.  Item =
 // (sequence b, key window, head group).  Each wave owns 16 query heads of the
 // group (their 576 query values in registers, 72 VGPRs) and computes complete
 // scores for them over every key (16x16x32 MFMAs), its own online softmax,
-// and all 512 value columns of its heads (16x16x16 MFMAs, P straight from the
-// score registers), so the key loop has no exchange between waves besides the
-// tile barrier.  Each wave reads the whole tile from LDS (K for the scores,
-// its first 512 columns transposed as the value operand); the cache is read
-// from memory once per head group.  Schedules (split, balanced) as in
-// mla_kernel.
-__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// and its share of the value columns of its heads (16x16x32 MFMAs over 32
+// keys, P straight from the score registers), so the key loop has no
+// exchange between waves besides the tile barrier.  Each wave reads the
+// tile's K and its value columns from LDS; the cache is read from memory once
+// per head group.  Schedules (split, balanced) as in mla_kernel.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void mla_hs_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[MlaHsLds::bytes];
-  int32_t* pcache = reinterpret_cast<int32_t*>(smem + MlaHsLds::pcache_off);
-  int* meta = reinterpret_cast<int*>(smem + MlaHsLds::pcache_off - 64);
+  using LD = typename MlaHsLayout<NW>::type;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
+  int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
+  int* meta = reinterpret_cast<int*>(smem + LD::pcache_off - 64);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (p.balanced) {
     const int HG = p.head_groups;
     const int w = blockIdx.x;
     int u0, u1, b, S;
-    if (!balanced_start<kDecWaves * kWave>(p, smem, meta, HG, u0, u1, b, S)) return;
+    if (!balanced_start<NW * kWave>(p, smem, meta, HG, u0, u1, b, S)) return;
     int u = u0;
     int piece = 0;
     while (u < u1) {
@@ -2838,7 +3087,7 @@ void mla_hs_kernel(AttnParams p) {
       const int klo = (u - a0) << kUnitShift;
       const int khi = min(L, (pu1 - a0) << kUnitShift);
       const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
-      mla_hs_item(p, smem, pcache, b, hg, L, klo, khi, slot, wave, lane);
+      mla_hs_item<NW>(p, smem, pcache, b, hg, L, klo, khi, slot, wave, lane);
       __syncthreads();                          // LDS is reused by the next piece
       u = pu1;
       ++piece;
@@ -2860,7 +3109,7 @@ void mla_hs_kernel(AttnParams p) {
   const int klo = split * p.split_keys;
   // the last window takes every remaining key
   const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
-  mla_hs_item(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
+  mla_hs_item<NW>(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -3227,12 +3476,11 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  const dim3 block(kDecWaves * kWave);
   // groups of up to 32 heads: column split (the waves share each score);
-  // 33 to 64: head split (16 heads per wave)
+  // 33 to 64: head split (16 heads per wave or wave pair)
   if (p.num_q_heads > 128 || p.group > 64 || p.group < 1) return hipErrorInvalidValue;
-  if (p.group <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, block, 0, stream, p);
-  else hipLaunchKernelGGL(mla_hs_kernel, grid, block, 0, stream, p);
+  if (p.group <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, dim3(kDecWaves * kWave), 0, stream, p);
+  else hipLaunchKernelGGL(mla_hs_kernel<kMlaHsWaves>, grid, dim3(kMlaHsWaves * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
