@@ -2576,22 +2576,8 @@ void mla_kernel(AttnParams p) {
   mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
 }
 
-// LDS of a head-split MLA workgroup: a ring of 32-key tiles, then the
-// page-id cache.
-struct MlaHsLds {
-  static constexpr int ring = 4;
-  static constexpr int pcache_off = ring * MlaGeo::tile_bytes + 64;
-  static constexpr int bytes = pcache_off + kPcacheEntries * 4;
-  static_assert(bytes <= kLdsMax, "MLA LDS budget exceeded");
-};
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 constexpr int kMlaHeads = 16;                    // query heads per wave
@@ -2601,8 +2587,8 @@ constexpr int kMlaVTilesHalf = kMlaLatent / 32;  // 16-wide value tiles in half 
 // Waves of a head-split MLA workgroup: eight, two per SIMD (waves w and
 // w + 4 share 16 heads and split each tile's keys for the scores and the
 // value columns for the output), so that one wave's LDS reads and softmax
-// overlap the other's MFMAs; with four, each wave takes all 512 columns of its
-// heads and runs alone on its SIMD.
+// overlap the other's MFMAs.  (One wave per SIMD holding all 512 columns of
+// its heads left every latency of the loop exposed.)
 constexpr int kMlaHsWaves = 8;
 
 // Running state of one wave: its 16 heads over its keys and NVT 16-wide value
@@ -2619,159 +2605,6 @@ __device__ __forceinline__ bf16x8 join_bf16x4(i16x4 lo, i16x4 hi) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
-}
-
-// One 32-key tile (LDS at kl; keys k0 .. k0 + 31, of which those >= khi are
-// masked) for this wave's 16 heads: scores S^T = K Q^T of both 16-key halves
-// on 16x16x32 MFMAs (lane l: head l % 16, keys 4 (l / 16) .. +3 of each
-// half), the online softmax over the eight keys a lane holds, and
-// O^T += V^T P^T for NVT value tiles from column col0 on 16x16x32 MFMAs with
-// the 32 keys as the contraction.  The contraction order is a permutation
-// of the keys: index 8 g + i is key 4 g + i for i < 4 and key 16 + 4 g + i - 4
-// otherwise, which is the order in which lane group g already holds its
-// probabilities (the B operand, straight from the score registers) and the
-// order two transposing LDS reads give the A operand (16-lane group g reads
-// keys 4 g .. 4 g + 3 of 16 columns from each half; lane L receives column
-// L's keys).
-template <bool CAP, int NVT>
-__device__ __forceinline__ void mla_tile(MlaState<NVT>& st, const uint8_t* kl, int k0, int khi,
-                                         const bf16x8 (&qreg)[kMlaQSteps], float c, const SoftCap& sc,
-                                         int col0, int lane) {
-  // every LDS operand read is issued one step ahead of the MFMAs that consume
-  // it (scheduling barriers keep that order)
-  constexpr int NP = kMlaQSteps / 2;            // pairs of score k-steps per half
-  constexpr int NI = 2 * NP;                    // score steps of the tile
-  constexpr int VG = 4;                         // value tiles per step
-  constexpr int half = 16 * MlaGeo::pitch;      // LDS offset of keys 16 .. 31
-  const uint8_t* krow = kl + (lane & 15) * MlaGeo::pitch + 16 * (lane >> 4);
-  const int L = lane & 15;
-  const uint8_t* vsrc = kl + (4 * (lane >> 4) + (L >> 2)) * MlaGeo::pitch + 8 * (L & 3) + 2 * col0;
-  f32x4 s[2][2];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) s[hb][0] = s[hb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 ka[NI][2];
-  ka[0][0] = *reinterpret_cast<const u32x4*>(krow);
-  ka[0][1] = *reinterpret_cast<const u32x4*>(krow + 64);
-#pragma unroll
-  for (int it = 0; it < NI; ++it) {
-    if (it + 1 < NI) {
-      const uint8_t* a = krow + ((it + 1) / NP) * half + 128 * ((it + 1) % NP);
-      ka[it + 1][0] = *reinterpret_cast<const u32x4*>(a);
-      ka[it + 1][1] = *reinterpret_cast<const u32x4*>(a + 64);
-    }
-    const int hb = it / NP, jp = it % NP;
-    s[hb][0] = mfma16_k32(as_bf16x8(ka[it][0]), qreg[2 * jp], s[hb][0]);
-    s[hb][1] = mfma16_k32(as_bf16x8(ka[it][1]), qreg[2 * jp + 1], s[hb][1]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the first value operands load while the softmax runs
-  i16x4 va[NVT / VG][VG][2];
-#pragma unroll
-  for (int u = 0; u < VG; ++u) {
-    va[0][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + 32 * u));
-    va[0][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vsrc + half + 32 * u));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  const int kb = k0 + 4 * (lane >> 4);
-  float v[8];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = s[hb][0][i] + s[hb][1][i];
-      if constexpr (CAP) x = cap1(x, sc);
-      v[4 * hb + i] = kb + 16 * hb + i < khi ? x : neg_inf();
-    }
-  float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, xor32(mx));
-  const float mxs = mx * c;
-  if (__builtin_amdgcn_ballot_w64(mxs > st.m + kRescaleSlack)) {
-    // rare (the running maximum grew by more than the slack): kept a branch,
-    // so that the accumulator is touched only here
-    __asm__ volatile("" ::: "memory");
-    const float m_new = fmaxf(st.m, mxs);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - (m_new == neg_inf() ? 0.f : m_new));
-    st.l *= alpha;
-#pragma unroll
-    for (int t = 0; t < NVT; ++t) st.o[t] *= alpha;
-    st.m = m_new;
-  }
-  const float nref = st.m == neg_inf() ? 0.f : -st.m;
-  float pr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], c, nref));
-  st.l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-  const bf16x8 pb = pack_bf16x8(pr);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int g = 0; g < NVT / VG; ++g) {
-    if (g + 1 < NVT / VG) {
-#pragma unroll
-      for (int u = 0; u < VG; ++u) {
-        const uint8_t* a = vsrc + 32 * (VG * (g + 1) + u);
-        va[g + 1][u][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
-        va[g + 1][u][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + half));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VG; ++u)
-      st.o[VG * g + u] = mfma16_k32(join_bf16x4(va[g][u][0], va[g][u][1]), pb, st.o[VG * g + u]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The key loop of a head-split MLA item: 32-key tiles of latent rows stream
-// through a ring of four LDS buffers by direct loads (issued three tiles
-// ahead, so that about 110 KB per compute unit are in flight; one barrier per
-// tile; the NW waves share each tile's loads).
-template <bool CAP, int NW, int NVT>
-__device__ __forceinline__ void mla_hs_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
-                                         int klo, int khi, const bf16x8 (&qreg)[kMlaQSteps], float c,
-                                         const SoftCap& sc, MlaState<NVT>& st, int col0, int wave, int lane) {
-  constexpr int R = MlaHsLds::ring;
-  using Loads = MlaLoads<NW>;
-  PageWalk w;
-  w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
-  w.page_bytes = p.kv_page_bytes;
-  w.head_off = 0;
-  w.row_stride_b = MlaGeo::row_bytes;
-  w.shift = p.page_shift;
-  w.klimit = L;
-  Loads ml;
-  ml.init(wave, lane);
-  const int chunk_keys = kPcacheEntries << w.shift;
-  for (int cb = klo; cb < khi; cb += chunk_keys) {
-    const int ce = min(khi, cb + chunk_keys);
-    __syncthreads();
-    fill_pcache(w, pcache, cb, ce);
-    wait_vmem_all();                            // Q loads and page-table reads
-    __syncthreads();
-    const int ntiles = (ce - cb + kSub - 1) / kSub;
-#pragma unroll
-    for (int t = 0; t < R - 1; ++t)
-      if (t < ntiles) ml.issue(p.k_pool, w, cb + t * kSub, smem + t * MlaGeo::tile_bytes, wave);
-    static_assert(R == 4, "the waits below count two tiles in flight");
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
-      // tile t must have landed; the (up to R-2) later tiles already issued
-      // may stay in flight (loads retire in order; each tile is at least
-      // min_per_wave loads of this wave)
-      const int ahead = min(R - 2, ntiles - 1 - t);
-      if (ahead >= 2)
-        wait_vmem<2 * Loads::min_per_wave>();
-      else if (ahead == 1)
-        wait_vmem<Loads::min_per_wave>();
-      else
-        wait_vmem<0>();
-      ring_barrier();
-      // the loads of tile t + R - 1 go into the buffer read in the previous
-      // iteration, which every wave has left (barrier above)
-      if (t + R - 1 < ntiles)
-        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
-      mla_tile<CAP, NVT>(st, smem + (t % R) * MlaGeo::tile_bytes, cb + t * kSub, khi, qreg, c, sc, col0, lane);
-    }
-  }
 }
 
 // LDS of a key-pair MLA workgroup: a ring of four 32-key tiles, the score
@@ -2813,10 +2646,16 @@ __device__ __forceinline__ f32x4 mla_half_scores(const uint8_t* kl, int kh, cons
 
 // The softmax of one 32-key tile (keys k0 .. k0 + 31, those >= khi masked)
 // from the scores of both halves (h0: keys 0 .. 15, h1: keys 16 .. 31, in
-// the score layout), then O^T += V^T P^T over NVT value tiles from column
-// col0, on 16x16x32 MFMAs with the tile's 32 keys as the contraction (key
-// order as in mla_tile).  Every wave of a pair runs the same operations on
-// the same values, so their running states stay equal.
+// the score layout: lane l holds head l % 16, keys 4 (l / 16) .. +3 of each
+// half), then O^T += V^T P^T over NVT value tiles from column col0, on
+// 16x16x32 MFMAs with the tile's 32 keys as the contraction.  The
+// contraction order is a permutation of the keys: index 8 g + i is key
+// 4 g + i for i < 4 and key 16 + 4 g + i - 4 otherwise, which is the order in
+// which lane group g already holds its eight probabilities (the B operand)
+// and in which two transposing LDS reads give the A operand (16-lane group g
+// reads keys 4 g .. 4 g + 3 of 16 columns from each half; lane L receives
+// column L's keys).  Every wave of a pair runs the same operations on the
+// same values, so their running states stay equal.
 template <bool CAP, int NVT>
 __device__ __forceinline__ void mla_tile_pv(MlaState<NVT>& st, const uint8_t* kl, int k0, int khi, f32x4 h0,
                                             f32x4 h1, float c, const SoftCap& sc, int col0, int lane) {
@@ -2965,16 +2804,15 @@ __device__ __forceinline__ void mla_pair_keys(const AttnParams& p, uint8_t* smem
 // hg (p.group heads starting at hg * p.group), then its outputs -- final rows
 // (slot < 0), a split-KV partial record (split schedule) or a balanced
 // partial record in slot `slot`.  Wave w takes heads 16 (w % 4) .. +15 of the
-// group and value columns [col0, col0 + 16 NVT) with col0 = 16 NVT (w / 4):
-// with eight waves, waves w and w + 4 compute the same scores and softmax
-// and each accumulates half of the 512 columns.
+// group, key half kh = w / 4 of every tile for the scores and value columns
+// [256 kh, 256 kh + 256) for the output.
 template <int NW>
 __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int hg, int L, int klo,
                             int khi, int slot, int wave, int lane) {
-  static_assert(NW == 4 || NW == 8, "four or eight waves");
-  constexpr int NVT = NW == 8 ? kMlaVTilesHalf : kMlaLatent / 16;
+  static_assert(NW == kMlaHsWaves, "two waves per SIMD");
+  constexpr int NVT = kMlaVTilesHalf;
   const int hl = (wave & 3) * kMlaHeads + (lane & 15);  // head within the group
-  const int kh = wave >> 2;                              // key half (eight waves)
+  const int kh = wave >> 2;                              // key half
   const int col0 = 16 * NVT * kh;
   const int h = hg * p.group + hl;
   const bool hok = hl < p.group && h < p.num_q_heads;
@@ -2997,17 +2835,10 @@ __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   st.m = neg_inf();
   st.l = 0.f;
   if (khi > klo) {
-    if constexpr (NW == 8) {
-      if (sc.on())
-        mla_pair_keys<true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
-      else
-        mla_pair_keys<false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
-    } else {
-      if (sc.on())
-        mla_hs_keys<true, NW, NVT>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, col0, wave, lane);
-      else
-        mla_hs_keys<false, NW, NVT>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, col0, wave, lane);
-    }
+    if (sc.on())
+      mla_pair_keys<true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
+    else
+      mla_pair_keys<false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, kh, col0, wave, lane);
   }
   // the row sum: this lane's keys, then the head's four lanes
   st.l += __shfl_xor(st.l, 16);
@@ -3037,28 +2868,18 @@ __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   }
 }
 
-template <int NW>
-struct MlaHsLayout {
-  using type = MlaHsLds;
-};
-template <>
-struct MlaHsLayout<8> {
-  using type = MlaPairLds;
-};
-
 // Head-split MLA decode, for head groups of 33 to 64 heads.  Item =
-// (sequence b, key window, head group).  Each wave owns 16 query heads of the
-// group (their 576 query values in registers, 72 VGPRs) and computes complete
-// scores for them over every key (16x16x32 MFMAs), its own online softmax,
-// and its share of the value columns of its heads (16x16x32 MFMAs over 32
-// keys, P straight from the score registers), so the key loop has no
-// exchange between waves besides the tile barrier.  Each wave reads the
-// tile's K and its value columns from LDS; the cache is read from memory once
-// per head group.  Schedules (split, balanced) as in mla_kernel.
+// (sequence b, key window, head group).  Each pair of waves owns 16 query
+// heads of the group (their 576 query values in registers, 72 VGPRs, in both
+// waves) and splits every tile's keys for the scores (16x16x32 MFMAs, swapped
+// through LDS) and the value columns for the output (16x16x32 MFMAs over the
+// tile's 32 keys, P straight from the score registers); see mla_pair_keys.
+// The cache is read from memory once per head group.  Schedules (split,
+// balanced) as in mla_kernel.
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void mla_hs_kernel(AttnParams p) {
-  using LD = typename MlaHsLayout<NW>::type;
+  using LD = MlaPairLds;
   __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
   int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
   int* meta = reinterpret_cast<int*>(smem + LD::pcache_off - 64);
