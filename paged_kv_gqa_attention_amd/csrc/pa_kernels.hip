@@ -2937,6 +2937,58 @@ void mla_hs_kernel(AttnParams p) {
 // split-KV merge: LSE = log sum exp(LSE_s), O = sum exp(LSE_s - LSE) O_s
 // ---------------------------------------------------------------------------
 
+// Running log-sum-exp combination of partial records (exp2 domain), taken
+// CH records at a time so that their loads are issued together: a merge row
+// costs one memory round trip per CH records instead of one for the maxima and
+// one per record.  A record whose LSE is -inf (an empty window) is skipped by
+// selects, since its O slots were never written.  With all records in one
+// chunk the arithmetic is the plain two-pass combination, in record order.
+template <int PER, int CH>
+struct MergeRow {
+  float acc[PER];
+  float wsum = 0.f, mx = neg_inf();
+
+  __device__ __forceinline__ MergeRow() {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  }
+
+  __device__ __forceinline__ void add(const float (&ls)[CH], const float (&v)[CH][PER]) {
+    float cm = mx;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ls[u]);
+    if (cm == neg_inf()) return;
+    if (cm != mx) {               // the first visible record sets mx; later growth rescales
+      const float a = __builtin_amdgcn_exp2f(mx - cm);
+      wsum *= a;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] *= a;
+      mx = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const bool live = ls[u] != neg_inf();
+      const float w = live ? __builtin_amdgcn_exp2f(ls[u] - mx) : 0.f;
+      wsum += w;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] = live ? acc[k] + w * v[u][k] : acc[k];
+    }
+  }
+
+  // bf16 O (lane's PER values) and natural-log LSE
+  __device__ __forceinline__ void store(uint16_t* dst, float* lse_dst) const {
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const __bf16 v = (__bf16)(acc[k] * inv);
+      dst[k] = __builtin_bit_cast(uint16_t, v);
+    }
+    if (lse_dst) *lse_dst = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+  }
+};
+
+constexpr int kMergeChunk = 4;        // partial records loaded together per merge row
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
@@ -2947,33 +2999,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int t = (int)(row / p.num_q_heads);
   const int h = (int)(row - (int64_t)t * p.num_q_heads);
   const int64_t plane = (int64_t)p.max_total_q * p.num_q_heads;
-  float mx = neg_inf();
-  for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.part_lse[s * plane + row]);
   constexpr int PER = D / 64;     // d values per lane
-  float acc[PER];
+  constexpr int CH = kMergeChunk;
+  MergeRow<PER, CH> m;
+  for (int s0 = 0; s0 < p.num_splits; s0 += CH) {
+    float ls[CH], v[CH][PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float wsum = 0.f;
-  if (mx != neg_inf()) {
-    for (int s = 0; s < p.num_splits; ++s) {
-      const float ls = p.part_lse[s * plane + row];
-      if (ls == neg_inf()) continue;
-      const float w = __builtin_amdgcn_exp2f(ls - mx);
-      wsum += w;
+    for (int u = 0; u < CH; ++u) {
+      const int s = min(s0 + u, p.num_splits - 1);     // past the last split: re-read it, unused
+      ls[u] = s0 + u < p.num_splits ? p.part_lse[s * plane + row] : neg_inf();
       const float* src = p.part_o + (s * plane + row) * D + lane * PER;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+      for (int k = 0; k < PER; ++k) v[u][k] = src[k];
     }
+    m.add(ls, v);
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + lane * PER;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const __bf16 v = (__bf16)(acc[k] * inv);
-    dst[k] = __builtin_bit_cast(uint16_t, v);
-  }
-  if (p.lse && lane == 0)
-    p.lse[row] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+  m.store(p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + lane * PER,
+          p.lse && lane == 0 ? p.lse + row : nullptr);
 }
 
 // Rows of balanced decode whose item was cut between workgroups: combine the
@@ -2996,6 +3038,7 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedMergeParams
   const int S = p.sched[4 + b];
   const int sb = p.sched[4 + b + 1] - S;
   constexpr int PER = D / 64;     // d values per lane
+  constexpr int CH = kMergeChunk;
   uint16_t* dst = p.out + (int64_t)t * p.o_stride_t + (int64_t)h * D + lane * PER;
   if (sb == 0) {                  // no visible key
 #pragma unroll
@@ -3006,35 +3049,21 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedMergeParams
   const int a0 = p.num_kv_heads * S + g * sb;
   const int w0 = a0 / U, w1 = (a0 + sb - 1) / U;
   if (w0 == w1) return;
-  float mx = neg_inf();
-  for (int wg = w0; wg <= w1; ++wg) {
-    const int slot = 2 * wg + ((wg == w0 && a0 != w0 * U) ? 1 : 0);
-    mx = fmaxf(mx, p.part_lse[(int64_t)slot * G + r]);
-  }
-  float acc[PER];
+  MergeRow<PER, CH> m;
+  for (int c0 = w0; c0 <= w1; c0 += CH) {
+    float ls[CH], v[CH][PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  float wsum = 0.f;
-  if (mx != neg_inf()) {
-    for (int wg = w0; wg <= w1; ++wg) {
+    for (int u = 0; u < CH; ++u) {
+      const int wg = min(c0 + u, w1);                  // past the last piece: re-read it, unused
       const int64_t rec = (int64_t)(2 * wg + ((wg == w0 && a0 != w0 * U) ? 1 : 0)) * G + r;
-      const float ls = p.part_lse[rec];
-      if (ls == neg_inf()) continue;
-      const float wt = __builtin_amdgcn_exp2f(ls - mx);
-      wsum += wt;
+      ls[u] = c0 + u <= w1 ? p.part_lse[rec] : neg_inf();
       const float* src = p.part_o + rec * D + lane * PER;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) acc[k] += wt * src[k];
+      for (int k = 0; k < PER; ++k) v[u][k] = src[k];
     }
+    m.add(ls, v);
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const __bf16 v = (__bf16)(acc[k] * inv);
-    dst[k] = __builtin_bit_cast(uint16_t, v);
-  }
-  if (p.lse && lane == 0)
-    p.lse[(int64_t)t * p.num_q_heads + h] = mx == neg_inf() ? neg_inf() : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+  m.store(dst, p.lse && lane == 0 ? p.lse + (int64_t)t * p.num_q_heads + h : nullptr);
 }
 
 // ---------------------------------------------------------------------------
