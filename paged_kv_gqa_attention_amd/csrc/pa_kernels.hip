@@ -122,6 +122,18 @@ struct Block {
 // ring filled by direct global->LDS loads.
 template <int D, bool FP8, int MODE>
 struct RingDec { static constexpr bool value = MODE == kDecode && D == 256 && FP8; };
+
+// The ring decode runs eight waves, two per SIMD (its query rows sit in LDS,
+// so that the 128-register accumulator fits the 256 registers of two waves);
+// every other instance has the shape of Block.
+constexpr int kRingWaves = 8;
+template <int D, bool FP8, int MODE, bool QF8 = false>
+struct Shape {
+  static constexpr bool ring = RingDec<D, FP8, MODE>::value;
+  static constexpr int waves = ring ? kRingWaves : Block<MODE, D, QF8>::waves;
+  static constexpr int threads = waves * kWave;
+  static constexpr int waves_per_eu = ring ? kRingWaves / 4 : Block<MODE, D, QF8>::waves_per_eu;
+};
 constexpr int kSub = 32;                  // keys per score tile (MFMA M of S^T)
 constexpr int kCols = 32;                 // packed query rows per wave (MFMA N)
 constexpr int kTile = 64;                 // keys per shared LDS tile (prefill schedule)
@@ -179,8 +191,10 @@ struct Geo {
 
 // Byte geometry of the ring decode.  A half-step is the K rows (or the V rows)
 // of 32 keys, unpadded; bank conflicts are avoided by storing 16-byte chunk c
-// of row r at chunk position c ^ (r mod 16).  Each wave owns four half-step
-// buffers (K and V of two steps), filled by direct global->LDS loads of 1 KB.
+// of row r at chunk position c ^ (r mod 16).  Each wave owns two half-step
+// buffers (K and V of one step), filled by direct global->LDS loads of 1 KB;
+// the block's 32 bf16 query rows follow the rings (padded rows, so that the
+// eight lanes of a 16-byte read hit distinct banks).
 template <int D, bool FP8>
 struct RingGeo {
   static constexpr int esz = FP8 ? 1 : 2;
@@ -188,16 +202,19 @@ struct RingGeo {
   static constexpr int chunks = row_bytes / 16;
   static constexpr int half_bytes = kSub * row_bytes;       // K (or V) rows of one step
   static constexpr int half_loads = half_bytes / 1024;      // direct loads per half-step
-  static constexpr int wave_bytes = 4 * half_bytes;         // K0, K1, V0, V1
-  static constexpr int ring_bytes = kDecWaves * wave_bytes;
+  static constexpr int wave_bytes = 2 * half_bytes;         // K, V
+  static constexpr int ring_bytes = kRingWaves * wave_bytes;
+  static constexpr int q_pitch = D * 2 + 16;
+  static constexpr int q_off = ring_bytes;
+  static constexpr int bytes = q_off + kCols * q_pitch;
   static_assert(chunks == 16, "one row is exactly the 16 swizzled chunks");
-  static_assert(ring_bytes + 64 + kPcacheEntries * 4 <= kLdsMax, "LDS budget of the ring");
+  static_assert(bytes + 64 + kPcacheEntries * 4 <= kLdsMax, "LDS budget of the ring");
 };
 
 template <int D, bool FP8, bool RING>
 struct RingBytes { static constexpr int bytes = 0; };
 template <int D, bool FP8>
-struct RingBytes<D, FP8, true> { static constexpr int bytes = RingGeo<D, FP8>::ring_bytes; };
+struct RingBytes<D, FP8, true> { static constexpr int bytes = RingGeo<D, FP8>::bytes; };
 
 template <int D, bool FP8, int MODE>
 struct Lds {
@@ -1643,19 +1660,22 @@ __device__ void merge_waves(SoftmaxState<D>& st, uint8_t* smem, int lds_avail, i
 }
 
 // One (sequence, KV head, key window [klo, khi)) item whose packed query rows
-// fit one MFMA column tile, on an fp8 cache at head dim 256.  Wave w takes the
-// 32-key steps w, w + 4, ... of the window.  Its private LDS holds the K and V
-// rows of two steps; the K rows of step s + 2 are requested as soon as the
-// score product of step s has read its K buffer, the V rows as soon as its PV
-// product has read the V buffer, so about three half-steps (24 KB) per wave
-// are in flight while it computes, with no register holding data in flight
-// and no workgroup barrier in the key loop.  Every step converts each fp8
-// byte once; the four waves' softmax states are merged at the end.
+// fit one MFMA column tile, on an fp8 cache at head dim 256.  Eight waves, two
+// per SIMD; wave w takes the 32-key steps w, w + 8, ... of the window.  The
+// block's query rows are staged once in LDS and read as the B operand of each
+// score k-step (in registers they would take 64 of the 256 registers two
+// waves per SIMD leave).  A wave's private LDS holds the K and V rows of one
+// step: the K rows of step s + 1 are requested as soon as the score product
+// of step s has read its K buffer, the V rows as soon as its PV product has
+// read the V buffer, with no register holding data in flight and no
+// workgroup barrier in the key loop; a wave waiting for its rows or for the
+// load path leaves its SIMD to the other wave.  Every step converts each fp8
+// byte once; the eight waves' softmax states are merged at the end.
 template <int D, bool FP8, int MODE>
 __device__ void ring_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, const RowMap& rm,
                           const PageWalk& pw, int L, int klo, int khi, int slot, float c, float vdesc) {
   using R = RingGeo<D, FP8>;
-  constexpr int NW = kDecWaves;
+  constexpr int NW = kRingWaves;
   constexpr int HL = R::half_loads;
   const SoftCap sc(p.softcap, c);
   const int lane = threadIdx.x & (kWave - 1);
@@ -1670,32 +1690,37 @@ __device__ void ring_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, c
     return;
   }
 
-  // query operands of the block's rows (zero past the last row), in registers
-  bf16x8 qreg[D / 16];
+  // the block's query rows (zero past the last row) into LDS: 32 rows of
+  // D / 8 16-byte chunks, two chunks per thread
+  uint8_t* qlds = smem + R::q_off;
   {
-    const int r = lane & 31;
-    const bool ok = r < nrows;
-    const int tok = ok ? r / rm.G : 0;
-    const int h = rm.g * rm.G + (r - tok * rm.G);
-    const uint16_t* src = p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + (lane >> 5) * 8;
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-      qreg[j] = ok ? as_bf16x8(*reinterpret_cast<const u32x4*>(src + 16 * j)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    constexpr int QCH = D / 8;
+    for (int i = threadIdx.x; i < kCols * QCH; i += NW * kWave) {
+      const int r = i / QCH, ch = i - r * QCH;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r < nrows) {
+        const int tok = r / rm.G;
+        const int h = rm.g * rm.G + (r - tok * rm.G);
+        v = *reinterpret_cast<const u32x4*>(p.q + (int64_t)(rm.t0 + tok) * p.q_stride_t + (int64_t)h * D + 8 * ch);
+      }
+      *reinterpret_cast<u32x4*>(qlds + r * R::q_pitch + 16 * ch) = v;
+    }
   }
+  // B operand of k-step j: row lane % 32, columns 16 j + 8 (lane / 32) .. +7
+  const uint8_t* qsrc = qlds + (lane & 31) * R::q_pitch + 16 * (lane >> 5);
   const int my_tok = min((lane & 31) / rm.G, max(rm.ntok - 1, 0));
   const int klim = p.causal ? min(khi, rm.pos0 + my_tok + 1) : khi;   // this lane's row sees keys < klim
   const int kfull = p.causal ? min(khi, rm.pos0 + 1) : khi;           // keys < kfull visible to every row
 
-  uint8_t* region = smem + wave * R::wave_bytes;       // K0, K1, V0, V1
+  uint8_t* kl = smem + wave * R::wave_bytes;           // K, then V
+  uint8_t* vl = kl + R::half_bytes;
   PageWalk w = pw;
   const int chunk_keys = kPcacheEntries << w.shift;
   for (int cb = klo; cb < khi; cb += chunk_keys) {
     const int ce = min(khi, cb + chunk_keys);
-    __syncthreads();                                     // the buffers and page cache are free
+    __syncthreads();                                     // the buffers and page cache are free; Q staged
     fill_pcache(w, pcache, cb, ce);
-    // the query loads (first chunk) overlapped the page-table reads; they
-    // retire here, once, so that no wait inside the loop covers them
-    wait_vmem_all();
+    wait_vmem_all();                                     // page-table reads
     __syncthreads();
     const int nsteps = (ce - cb + kSub - 1) / kSub;
     const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;   // this wave's steps
@@ -1704,33 +1729,38 @@ __device__ void ring_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, c
       // last key): every iteration then has the same loads in flight and the
       // same wait counts.
       auto key_of = [&](int i) { return cb + kSub * min(wave + NW * i, nsteps - 1); };
-      ring_issue<D, FP8>(p.k_pool, w, key_of(0), region, lane);
-      ring_issue<D, FP8>(p.v_pool, w, key_of(0), region + 2 * R::half_bytes, lane);
-      ring_issue<D, FP8>(p.k_pool, w, key_of(1), region + R::half_bytes, lane);
-      ring_issue<D, FP8>(p.v_pool, w, key_of(1), region + 3 * R::half_bytes, lane);
+      ring_issue<D, FP8>(p.k_pool, w, key_of(0), kl, lane);
+      ring_issue<D, FP8>(p.v_pool, w, key_of(0), vl, lane);
       for (int i = 0; i < mine; ++i) {
         const int key0 = cb + kSub * (wave + NW * i);
-        const uint8_t* kl = region + (i & 1) * R::half_bytes;
-        const uint8_t* vl = region + (2 + (i & 1)) * R::half_bytes;
-        wait_vmem<3 * HL>();                             // K(i) landed; V(i), K(i+1), V(i+1) may fly
+        // the operand addresses (swizzled per lane) are recomputed every step
+        // from an opaque copy of the lane id: hoisted, they would hold some
+        // 32 registers for the whole kernel
+        const int ln = item_tid() & (kWave - 1);
+        wait_vmem<HL>();                                 // K(i) landed; V(i) may fly
         f32x16 sv[1];
 #pragma unroll
         for (int e = 0; e < 16; ++e) sv[0][e] = 0.f;
+        u32x4 qb = *reinterpret_cast<const u32x4*>(qsrc);
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) sv[0] = mfma32(k_operand_r<D, FP8>(kl, j, lane), qreg[j], sv[0]);
+        for (int j = 0; j < D / 16; ++j) {
+          const u32x4 qn = j + 1 < D / 16 ? *reinterpret_cast<const u32x4*>(qsrc + 32 * (j + 1)) : qb;
+          sv[0] = mfma32(k_operand_r<D, FP8>(kl, j, ln), as_bf16x8(qb), sv[0]);
+          qb = qn;
+        }
         __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the K reads have returned
-        ring_issue<D, FP8>(p.k_pool, w, key_of(i + 2), region + (i & 1) * R::half_bytes, lane);
+        ring_issue<D, FP8>(p.k_pool, w, key_of(i + 1), kl, lane);
         if (sc.on()) cap_tile(sv[0], sc);
         if (key0 + kSub > kfull) mask_tile(sv[0], key0, klim, lane);
-        wait_vmem<3 * HL>();                             // V(i) landed; K(i+1), V(i+1), K(i+2) may fly
+        wait_vmem<HL>();                                 // V(i) landed; K(i+1) may fly
         bf16x8 pb[1][2];
         softmax_p<D, 1>(st, sv, c, pb);
 #pragma unroll
         for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) st.o[t] = mfma32(v_operand_r<D, FP8>(vl, t, h, lane), pb[0][h], st.o[t]);
+          for (int h = 0; h < 2; ++h) st.o[t] = mfma32(v_operand_r<D, FP8>(vl, t, h, ln), pb[0][h], st.o[t]);
         __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): the V reads have returned
-        ring_issue<D, FP8>(p.v_pool, w, key_of(i + 2), region + (2 + (i & 1)) * R::half_bytes, lane);
+        ring_issue<D, FP8>(p.v_pool, w, key_of(i + 1), vl, lane);
       }
       wait_vmem_all();                                   // nothing lands in the buffers later
     }
@@ -1871,7 +1901,7 @@ __device__ void balanced_decode(const AttnParams& p, uint8_t* smem, int32_t* pca
   const int Hkv = p.num_kv_heads;
   const int w = blockIdx.x;
   int u0, u1, b, S;
-  if (!balanced_start<Block<MODE, D>::threads>(p, smem, meta, Hkv, u0, u1, b, S)) return;
+  if (!balanced_start<Shape<D, FP8, MODE>::threads>(p, smem, meta, Hkv, u0, u1, b, S)) return;
   float c, vdesc;
   score_scales<FP8>(p, c, vdesc);
   int u = u0;
@@ -2071,8 +2101,8 @@ __global__ __launch_bounds__(1024) void queue_setup_kernel(QueueSetupParams q) {
 // mixed batch (its own instance, so that its loop does not change the
 // register allocation of the one-item-per-workgroup kernel).
 template <int D, bool FP8, int MODE, bool QF8 = false, bool QUEUE = false>
-__global__ __launch_bounds__((Block<MODE, D, QF8>::threads))
-__attribute__((amdgpu_waves_per_eu(Block<MODE, D, QF8>::waves_per_eu, Block<MODE, D, QF8>::waves_per_eu)))
+__global__ __launch_bounds__((Shape<D, FP8, MODE, QF8>::threads))
+__attribute__((amdgpu_waves_per_eu(Shape<D, FP8, MODE, QF8>::waves_per_eu, Shape<D, FP8, MODE, QF8>::waves_per_eu)))
 void attn_kernel(AttnParams p) {
   static_assert(!QF8 || (FP8 && MODE == kPrefill && Block<MODE, D>::stream), "fp8 queries: streamed fp8 prefill only");
   static_assert(!QUEUE || MODE == kMixed, "task queues: mixed batches only");
@@ -2201,9 +2231,9 @@ struct MlaGeo {
 
 // Direct global->LDS loads of one 32-key tile: load i writes slots
 // [64 i, 64 i + 64) of the tile; lane l fetches the 16 bytes that belong at
-// slot 64 i + l (a pad slot, or a slot past the 32 rows, re-fetches chunk 0 of
-// row 31: in bounds, never read).  Loader wave w of NW issues loads w,
-// w + NW, ...
+// slot 64 i + l (a pad slot re-fetches chunk 0 of its row, a slot past the 32
+// rows chunk 0 of row 31: in bounds, never read).  Loader wave w of NW issues
+// loads w, w + NW, ...
 template <int NW>
 struct MlaLoads {
   static constexpr int per_wave = (MlaGeo::loads + NW - 1) / NW;
@@ -3223,7 +3253,7 @@ hipError_t launch_one(const AttnParams& p, dim3 grid, hipStream_t stream) {
     }
   }
   if (p.queue) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Block<MODE, D>::threads), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<D, FP8, MODE>), grid, dim3(Shape<D, FP8, MODE>::threads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -3263,7 +3293,7 @@ hipError_t launch_attention(int head_dim, bool kv_fp8, Mode mode, const AttnPara
 template <int D, bool FP8, int MODE>
 constexpr int wgs_per_cu() {
   constexpr int by_lds = kLdsMax / Lds<D, FP8, MODE>::bytes;
-  constexpr int by_waves = Block<MODE, D>::waves_per_eu * 4 / Block<MODE, D>::waves;   // 4 SIMDs per CU
+  constexpr int by_waves = Shape<D, FP8, MODE>::waves_per_eu * 4 / Shape<D, FP8, MODE>::waves;   // 4 SIMDs per CU
   constexpr int n = by_lds < by_waves ? by_lds : by_waves;
   return n > 0 ? n : 1;
 }
