@@ -2290,320 +2290,10 @@ struct MlaLoads {
   }
 };
 
-// LDS of an MLA workgroup with NCT row tiles: the exchange buffer for the
-// waves' partial scores, then as many tile buffers as fit.
-template <int NCT>
-struct MlaLds {
-  static constexpr int xbuf_bytes = kDecWaves * NCT * 4 * kWave * 16;   // partial scores
-  static constexpr int pbuf_bytes = NCT * 2 * kWave * 16;               // bf16 probabilities
-  static constexpr int mbuf_bytes = NCT * kWave * 16;                   // per-wave row maxima
-  static constexpr int ring = (kLdsMax - 64 - kPcacheEntries * 4 - xbuf_bytes - pbuf_bytes - mbuf_bytes) /
-                              MlaGeo::tile_bytes;
-  static constexpr int xbuf_off = ring * MlaGeo::tile_bytes;
-  static constexpr int pbuf_off = xbuf_off + xbuf_bytes;
-  static constexpr int mbuf_off = pbuf_off + pbuf_bytes;
-  static constexpr int pcache_off = mbuf_off + mbuf_bytes + 64;
-  static constexpr int bytes = pcache_off + kPcacheEntries * 4;
-  static_assert(ring >= 2 && bytes <= kLdsMax, "MLA LDS budget exceeded");
-};
-
 // One soft-capped value (same formula as cap_tile).
 __device__ __forceinline__ float cap1(float x, const SoftCap& sc) {
   const float e = __builtin_amdgcn_exp2f(x * sc.k2);
   return __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(e + 1.f), 1.f) * sc.inv_b;
-}
-
-// The key loop of an MLA item (see mla_kernel).  CAP selects soft-capping at
-// compile time so that uncapped runs carry none of its work.
-template <int NCT, bool CAP>
-__device__ __forceinline__ void mla_keys(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int L,
-                                         int klo, int khi, const bf16x8 (&qreg)[NCT][kMlaDk / 16 / kDecWaves],
-                                         float c, const SoftCap& sc,
-                                         SoftmaxState<kMlaLatent / kDecWaves> (&st)[NCT], int wave, int lane) {
-  using LD = MlaLds<NCT>;
-  constexpr int R = LD::ring;
-  constexpr int QJ = kMlaDk / 16 / kDecWaves;       // score k-steps per wave
-  constexpr int VT = kMlaLatent / 32 / kDecWaves;   // value tiles per wave
-  uint8_t* xbuf = smem + LD::xbuf_off;
-  uint8_t* pbuf = smem + LD::pbuf_off;
-  uint8_t* mbuf = smem + LD::mbuf_off;
-  PageWalk w;
-  w.pt_row = p.page_table + (int64_t)b * p.pt_row_stride;
-  w.page_bytes = p.kv_page_bytes;
-  w.head_off = 0;
-  w.row_stride_b = MlaGeo::row_bytes;
-  w.shift = p.page_shift;
-  w.klimit = L;
-  MlaLoads<kDecWaves> ml;
-  ml.init(wave, lane);
-  const int chunk_keys = kPcacheEntries << w.shift;
-  for (int cb = klo; cb < khi; cb += chunk_keys) {
-    const int ce = min(khi, cb + chunk_keys);
-    __syncthreads();
-    fill_pcache(w, pcache, cb, ce);
-    wait_vmem_all();                            // Q loads and page-table reads
-    __syncthreads();
-    const int ntiles = (ce - cb + kSub - 1) / kSub;
-#pragma unroll
-    for (int t = 0; t < R - 1; ++t)
-      if (t < ntiles) ml.issue(p.k_pool, w, cb + t * kSub, smem + t * MlaGeo::tile_bytes, wave);
-#pragma unroll 1
-    for (int t = 0; t < ntiles; ++t) {
-      // tile t must have landed; up to R-2 later tiles may stay in flight
-      if (R >= 3 && t + 1 < ntiles)
-        wait_vmem<(R >= 3 ? MlaLoads<kDecWaves>::min_per_wave : 0)>();
-      else
-        wait_vmem<0>();
-      ring_barrier();
-      const uint8_t* kl = smem + (t % R) * MlaGeo::tile_bytes;
-      // partial scores over this wave's columns
-      f32x16 s[NCT];
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[rt][i] = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < QJ; ++jj) {
-        const bf16x8 a = k_operand<kMlaDk, false, MlaGeo::pitch>(kl, 0, QJ * wave + jj, lane);
-#pragma unroll
-        for (int rt = 0; rt < NCT; ++rt) s[rt] = mfma32(a, qreg[rt][jj], s[rt]);
-      }
-      // the next loads are issued while the score MFMAs run (the buffer they
-      // fill was last read in the previous iteration, before the barrier)
-      if (t + R - 1 < ntiles)
-        ml.issue(p.k_pool, w, cb + (t + R - 1) * kSub, smem + ((t + R - 1) % R) * MlaGeo::tile_bytes, wave);
-      // reduce-scatter of the partial scores: 16-byte records
-      // [source wave][row tile][quarter][lane]; wave w sums quarter w (elements
-      // 4 w .. 4 w + 3 of every lane) over the four sources in a fixed order
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(xbuf + (((wave * NCT + rt) * 4 + q4) * kWave + lane) * 16) =
-              f32x4{s[rt][4 * q4], s[rt][4 * q4 + 1], s[rt][4 * q4 + 2], s[rt][4 * q4 + 3]};
-      ring_barrier();
-      const int k0 = cb + t * kSub;
-      f32x4 g4[NCT];
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt) {
-        g4[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w2 = 0; w2 < kDecWaves; ++w2)
-          g4[rt] += *reinterpret_cast<const f32x4*>(xbuf + (((w2 * NCT + rt) * 4 + wave) * kWave + lane) * 16);
-        // this quarter's keys past the window are masked; soft cap if asked
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = g4[rt][e];
-          if constexpr (CAP) v = cap1(v, sc);
-          g4[rt][e] = k0 + acc_key(4 * wave + e, lane) < khi ? v : neg_inf();
-        }
-        // this wave's part of the row maximum (both lane halves hold the row)
-        float mx = fmaxf(fmaxf(g4[rt][0], g4[rt][1]), fmaxf(g4[rt][2], g4[rt][3]));
-        mx = fmaxf(mx, xor32(mx));
-        reinterpret_cast<float*>(mbuf)[(rt * kWave + lane) * 4 + wave] = mx;
-      }
-      ring_barrier();
-      // Softmax split over the waves: every wave forms the same row maximum
-      // and running state, the probabilities of its quarter and its own
-      // partial row sum; the bf16 probabilities meet in LDS as the PV operand.
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt) {
-        const f32x4 m4 = *reinterpret_cast<const f32x4*>(mbuf + (rt * kWave + lane) * 16);
-        const float mxs = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * c;
-        if (__builtin_amdgcn_ballot_w64(mxs > st[rt].m + kRescaleSlack)) {
-          const float m_new = fmaxf(st[rt].m, mxs);
-          const float alpha = __builtin_amdgcn_exp2f(st[rt].m - (m_new == neg_inf() ? 0.f : m_new));
-          st[rt].l *= alpha;
-#pragma unroll
-          for (int tt = 0; tt < VT; ++tt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) st[rt].o[tt][i] *= alpha;
-          st[rt].m = m_new;
-        }
-        const float nref = st[rt].m == neg_inf() ? 0.f : -st[rt].m;
-        float pq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pq[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(g4[rt][e], c, nref));
-        st[rt].l += (pq[0] + pq[1]) + (pq[2] + pq[3]);
-        *reinterpret_cast<u32x2*>(pbuf + ((rt * 2 + (wave >> 1)) * kWave + lane) * 16 + (wave & 1) * 8) =
-            u32x2{pack_bf16x2(pq[0], pq[1]), pack_bf16x2(pq[2], pq[3])};
-      }
-      ring_barrier();
-      bf16x8 pb[NCT][2];
-#pragma unroll
-      for (int rt = 0; rt < NCT; ++rt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          pb[rt][hh] = as_bf16x8(*reinterpret_cast<const u32x4*>(pbuf + ((rt * 2 + hh) * kWave + lane) * 16));
-      // O^T += V^T P^T over this wave's value columns of the same tile
-#pragma unroll
-      for (int tt = 0; tt < VT; ++tt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 a = v_operand<false, MlaGeo::pitch>(kl, 0, VT * wave + tt, hh, lane);
-#pragma unroll
-          for (int rt = 0; rt < NCT; ++rt) st[rt].o[tt] = mfma32(a, pb[rt][hh], st[rt].o[tt]);
-        }
-    }
-  }
-}
-
-// One MLA item: the keys [klo, khi) of sequence b for head group hg, then its
-// outputs -- final rows (slot < 0), a split-KV partial record (split
-// schedule) or a balanced partial record in slot `slot`.
-template <int NCT>
-__device__ void mla_item(const AttnParams& p, uint8_t* smem, int32_t* pcache, int b, int hg, int L, int klo,
-                         int khi, int slot, int wave, int lane) {
-  using LD = MlaLds<NCT>;
-  constexpr int QJ = kMlaDk / 16 / kDecWaves;
-  constexpr int VT = kMlaLatent / 32 / kDecWaves;
-  // this wave's query columns of every row tile
-  bf16x8 qreg[NCT][QJ];
-#pragma unroll
-  for (int rt = 0; rt < NCT; ++rt) {
-    const int h = (hg * NCT + rt) * kCols + (lane & 31);
-    const bool ok = h < p.num_q_heads;
-    const uint16_t* src = p.q + (int64_t)b * p.q_stride_t + (int64_t)(ok ? h : 0) * kMlaDk +
-                          16 * QJ * wave + (lane >> 5) * 8;
-#pragma unroll
-    for (int jj = 0; jj < QJ; ++jj) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * jj);
-      qreg[rt][jj] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
-    }
-  }
-  float c, vdesc;
-  score_scales<false>(p, c, vdesc);
-  const SoftCap sc(p.softcap, c);
-  SoftmaxState<VT * 32> st[NCT];
-#pragma unroll
-  for (int rt = 0; rt < NCT; ++rt) state_init(st[rt]);
-  if (khi > klo) {
-    if (sc.on())
-      mla_keys<NCT, true>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
-    else
-      mla_keys<NCT, false>(p, smem, pcache, b, L, klo, khi, qreg, c, sc, st, wave, lane);
-  }
-  // full row sums: each wave holds the sum over its quarter of the keys
-  float* lsum = reinterpret_cast<float*>(smem + LD::xbuf_off);
-  __syncthreads();
-#pragma unroll
-  for (int rt = 0; rt < NCT; ++rt) lsum[(wave * NCT + rt) * kWave + lane] = st[rt].l + xor32(st[rt].l);
-  __syncthreads();
-  const int d_base = VT * 32 * wave;
-#pragma unroll
-  for (int rt = 0; rt < NCT; ++rt) {
-    const int h = (hg * NCT + rt) * kCols + (lane & 31);
-    float l_tot = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kDecWaves; ++w2) l_tot += lsum[(w2 * NCT + rt) * kWave + lane];
-    if (h >= p.num_q_heads) continue;
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : vdesc / l_tot;
-    const float lse2 = empty ? neg_inf() : st[rt].m + __builtin_amdgcn_logf(l_tot);
-    if (slot >= 0) {
-      // balanced records hold the group's rows (p.group of them) per slot
-      const int64_t row = p.balanced ? (int64_t)slot * p.group + (h - hg * NCT * kCols)
-                                     : ((int64_t)slot * p.max_total_q + b) * p.num_q_heads + h;
-      if (wave == 0 && (lane >> 5) == 0) p.part_lse[row] = lse2;
-      if (empty) continue;
-      float* dst = p.part_o + row * kMlaLatent + d_base;
-#pragma unroll
-      for (int tt = 0; tt < VT; ++tt)
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
-          f32x4 v;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = st[rt].o[tt][4 * ig + k] * inv;
-          *reinterpret_cast<f32x4*>(dst + d0) = v;
-        }
-    } else {
-      uint16_t* dst = p.out + (int64_t)b * p.o_stride_t + (int64_t)h * kMlaLatent + d_base;
-#pragma unroll
-      for (int tt = 0; tt < VT; ++tt)
-#pragma unroll
-        for (int ig = 0; ig < 4; ++ig) {
-          const int d0 = 32 * tt + 8 * ig + (lane >> 5) * 4;
-          const u32x2 v{pack_bf16x2(st[rt].o[tt][4 * ig] * inv, st[rt].o[tt][4 * ig + 1] * inv),
-                        pack_bf16x2(st[rt].o[tt][4 * ig + 2] * inv, st[rt].o[tt][4 * ig + 3] * inv)};
-          *reinterpret_cast<u32x2*>(dst + d0) = v;
-        }
-      if (p.lse && wave == 0 && (lane >> 5) == 0) p.lse[(int64_t)b * p.num_q_heads + h] = lse2 * kLn2;
-    }
-  }
-}
-
-// MLA decode.  Item = (sequence b, key window, head group of up to 64 query
-// heads), NCT 32-row tiles of query heads.  The four waves split the work by
-// columns: wave w contracts columns [144 w, 144 w + 144) of q.C for every row
-// tile (its 36 query values per row in registers), the partial scores are
-// summed through LDS so that every wave holds the same full scores, the
-// softmax is split four ways (mla_keys), and wave w accumulates the value
-// columns [128 w, 128 w + 128).  No product is computed twice.  More than 64
-// heads take several head groups (their score and accumulator registers
-// would not fit one wave).  Used for groups of up to 32 heads (NCT = 1);
-// larger groups run mla_hs_kernel.
-//   Split schedule: one workgroup per (b, window, group); items are ordered
-//   (b, split, group) and dealt so that each XCD takes a contiguous run of
-//   them, which puts the head groups of one window on one L2.
-//   Balanced schedule (p.balanced): one workgroup per compute unit, each
-//   taking an equal run of 128-key units over all (b, group) items laid end
-//   to end (balanced_start), piece by piece; cut pieces become partial
-//   records for merge_balanced_kernel.
-template <int NCT>
-__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_kernel(AttnParams p) {
-  using LD = MlaLds<NCT>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LD::bytes];
-  int32_t* pcache = reinterpret_cast<int32_t*>(smem + LD::pcache_off);
-  int* meta = reinterpret_cast<int*>(smem + LD::pcache_off - 64);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (p.balanced) {
-    const int HG = p.head_groups;
-    const int w = blockIdx.x;
-    int u0, u1, b, S;
-    if (!balanced_start<kDecWaves * kWave>(p, smem, meta, HG, u0, u1, b, S)) return;
-    int u = u0;
-    int piece = 0;
-    while (u < u1) {
-      const int sb = seq_units(p, b);
-      const int item0 = HG * S;
-      if (sb == 0 || u >= item0 + HG * sb) {    // past this sequence's items
-        S += sb;
-        ++b;
-        continue;
-      }
-      const int hg = (u - item0) / sb;
-      const int a0 = item0 + hg * sb;
-      const int a1 = a0 + sb;
-      const int pu1 = min(u1, a1);
-      const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
-      const int klo = (u - a0) << kUnitShift;
-      const int khi = min(L, (pu1 - a0) << kUnitShift);
-      const int slot = (u == a0 && pu1 == a1) ? -1 : 2 * w + (piece == 0 ? 0 : 1);
-      mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, slot, wave, lane);
-      u = pu1;
-      ++piece;
-    }
-    return;
-  }
-  int hg, b, split;
-  {
-    const int n = gridDim.x;
-    const int lin = blockIdx.x;
-    const int full = n - n % kXcds;
-    const int logical = lin < full ? (lin % kXcds) * (full / kXcds) + lin / kXcds : lin;
-    hg = logical % p.head_groups;
-    const int rest = logical / p.head_groups;
-    split = rest % p.num_splits;
-    b = rest / p.num_splits;
-  }
-  const int L = min(p.seq_lens[b], p.pt_cols << p.page_shift);
-  const int klo = split * p.split_keys;
-  // the last window takes every remaining key
-  const int khi = split == p.num_splits - 1 ? L : min(L, klo + p.split_keys);
-  mla_item<NCT>(p, smem, pcache, b, hg, L, klo, khi, p.num_splits > 1 ? split : -1, wave, lane);
 }
 
 __device__ __forceinline__ f32x4 mfma16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -2898,14 +2588,23 @@ __device__ void mla_hs_item(const AttnParams& p, uint8_t* smem, int32_t* pcache,
   }
 }
 
-// Head-split MLA decode, for head groups of 33 to 64 heads.  Item =
-// (sequence b, key window, head group).  Each pair of waves owns 16 query
-// heads of the group (their 576 query values in registers, 72 VGPRs, in both
-// waves) and splits every tile's keys for the scores (16x16x32 MFMAs, swapped
-// through LDS) and the value columns for the output (16x16x32 MFMAs over the
-// tile's 32 keys, P straight from the score registers); see mla_pair_keys.
-// The cache is read from memory once per head group.  Schedules (split,
-// balanced) as in mla_kernel.
+// MLA decode.  Item = (sequence b, key window, head group of up to 64 query
+// heads).  Each pair of waves owns 16 query heads of the group (their 576
+// query values in registers, 72 VGPRs, in both waves) and splits every tile's
+// keys for the scores (16x16x32 MFMAs, swapped through LDS) and the value
+// columns for the output (16x16x32 MFMAs over the tile's 32 keys, P straight
+// from the score registers); see mla_pair_keys.  A group of at most 48 heads
+// leaves pairs without live heads, which still share the tile loads and the
+// barriers (each pair has its own SIMD, so they cost the others nothing).
+// More than 64 heads take several head groups; the cache is read from memory
+// once per head group.
+//   Split schedule: one workgroup per (b, window, group); items are ordered
+//   (b, split, group) and dealt so that each XCD takes a contiguous run of
+//   them, which puts the head groups of one window on one L2.
+//   Balanced schedule (p.balanced): one workgroup per compute unit, each
+//   taking an equal run of 128-key units over all (b, group) items laid end
+//   to end (balanced_start), piece by piece; cut pieces become partial
+//   records for merge_balanced_kernel.
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void mla_hs_kernel(AttnParams p) {
@@ -3356,11 +3055,8 @@ hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
 
 hipError_t launch_mla(const AttnParams& p, dim3 grid, hipStream_t stream) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  // groups of up to 32 heads: column split (the waves share each score);
-  // 33 to 64: head split (16 heads per wave or wave pair)
   if (p.num_q_heads > 128 || p.group > 64 || p.group < 1) return hipErrorInvalidValue;
-  if (p.group <= 32) hipLaunchKernelGGL(mla_kernel<1>, grid, dim3(kDecWaves * kWave), 0, stream, p);
-  else hipLaunchKernelGGL(mla_hs_kernel<kMlaHsWaves>, grid, dim3(kMlaHsWaves * kWave), 0, stream, p);
+  hipLaunchKernelGGL(mla_hs_kernel<kMlaHsWaves>, grid, dim3(kMlaHsWaves * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
