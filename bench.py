@@ -326,6 +326,43 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def mfma_ceiling(iters: int = 1000, launches: int = 10):
+    """Sustained dense bf16 MFMA rate of this GPU (pa_calibrate_mfma): three
+    waves per SIMD doing nothing but v_mfma_f32_32x32x16_bf16, on random
+    N(0,1) bf16 operands and, for comparison, on zeros (the chip's clock under
+    a matrix-core load depends on how much the operand bits toggle).  The
+    random-operand rate is the practical ceiling of the MFMA-bound lines; their
+    roofline fractions stay taken against the published peak."""
+    import torch
+    from paged_kv_gqa_attention_amd import binding
+    # 136 VGPRs per wave: three 4-wave workgroups per CU, all resident at once
+    nwg = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    res = {}
+    for kind in ("random", "zeros"):
+        ops = torch.randn(nwg * 32768, generator=gen, device="cuda").to(torch.bfloat16)
+        if kind == "zeros":
+            ops.zero_()
+        sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+        stream = binding.current_stream()
+        for _ in range(2):
+            binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(launches):
+            binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / launches
+        res[kind] = binding.pa_calibrate_mfma_flops(nwg, iters) / (ms * 1e-3) / 1e12
+    return {"tflops": round(res["random"], 1), "frac_of_peak": round(res["random"] / BF16_PEAK_TFLOPS, 4),
+            "zero_operand_tflops": round(res["zeros"], 1),
+            "kernel": "pa_calibrate_mfma: v_mfma_f32_32x32x16_bf16 only, 3 waves per SIMD",
+            "operands": "random N(0,1) bf16 (zero_operand_tflops: all zeros)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +378,8 @@ def main():
                     help="query dtype for --only (fp8_e4m3 needs an fp8 cache, prefill)")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="plan num_splits for --only (0 heuristic, -1 balanced decode)")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="measure the sustained bf16 MFMA rate on random operands and print it")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -368,6 +407,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "repeats": 5}), flush=True)
+        return
+    if a.calibrate_mfma:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling()}), flush=True)
         return
     cpu_leg = not a.no_cpu
     if a.only:
@@ -453,6 +495,11 @@ def main():
                     "unit": "GB/s", "frac": round(e["alg_gbs"] / HBM_PEAK_GBS, 4)}
         roof.update(read_counters(name))
         e["roofline"] = roof
+    ceiling = mfma_ceiling() if sec else None
+    if ceiling:
+        for e in sec.values():
+            if e["roofline"]["unit"] == "TFLOP/s" and e["roofline"]["peak"] == BF16_PEAK_TFLOPS:
+                e["roofline"]["frac_of_mfma_ceiling"] = round(e["roofline"]["achieved"] / ceiling["tflops"], 4)
     w = prim["w"]
     alg_bytes = prim["kv_bytes"] + prim["qo_bytes"]
     achieved = alg_bytes / (prim["ms_per_step"] * 1e-3) / 1e9
@@ -485,6 +532,7 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
         "secondary": sec,
+        "mfma_ceiling": ceiling,
     }
     print(json.dumps(line), flush=True)
 

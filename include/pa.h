@@ -442,6 +442,29 @@ void pa_mla_plan_destroy(pa_mla_plan_t plan);
 /* Static string naming a status code. */
 const char* pa_status_str(pa_status status);
 
+/* ---------------------------------------------------------------------------
+ * Measurement (not part of the attention path)
+ *
+ * The roofline fractions of the prefill lines are taken against the published
+ * dense bf16 MFMA peak; these two calls measure the rate this GPU actually
+ * sustains when it does nothing but bf16 MFMAs (v_mfma_f32_32x32x16_bf16) on
+ * random operands, the practical ceiling of any MFMA-bound kernel here.  The
+ * score and PV products they stand for are the dense contractions of the
+ * attention definition (vLLM PR #48156, "Residual warmed gap": kernel time
+ * attributed by microbenchmark).
+ *   operands  device, 16-byte aligned, num_workgroups * 32768 bf16 values
+ *             (4 waves x 16 operands x 64 lanes x 8 values per workgroup),
+ *             read once; the caller fills them (random values for the ceiling)
+ *   sink      device, num_workgroups * 256 floats, written (the accumulators'
+ *             sums, so that no product is dead code)
+ *   iters     loop trips; each wave issues 64 MFMAs per trip
+ * Errors: PA_ERR_INVALID for null or misaligned pointers or non-positive
+ * sizes, PA_ERR_HIP when the launch fails.  pa_calibrate_mfma_flops returns
+ * the floating-point operations one such launch performs. */
+pa_status pa_calibrate_mfma(const uint16_t* operands, float* sink, int32_t num_workgroups, int32_t iters,
+                            hipStream_t stream);
+double pa_calibrate_mfma_flops(int32_t num_workgroups, int32_t iters);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ PA_Q_FP8_E4M3 = 1
 EXPORTS = ("pa_plan", "pa_workspace_bytes", "pa_plan_get_info", "pa_run_prefill",
            "pa_run_decode", "pa_run_mixed", "pa_run_append", "pa_plan_destroy", "pa_status_str",
            "pa_mla_plan", "pa_mla_workspace_bytes", "pa_mla_num_splits", "pa_run_mla_decode",
-           "pa_mla_plan_destroy", "pa_check_metadata", "pa_run_decode_static")
+           "pa_mla_plan_destroy", "pa_check_metadata", "pa_run_decode_static",
+           "pa_calibrate_mfma", "pa_calibrate_mfma_flops")
 
 PA_CHECK_PAGE_ID = 1
 PA_CHECK_Q_LEN = 2
@@ -206,6 +207,10 @@ def lib():
         L.pa_run_mla_decode.restype = ctypes.c_int
         L.pa_mla_plan_destroy.argtypes = [vp]
         L.pa_mla_plan_destroy.restype = None
+        L.pa_calibrate_mfma.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
+        L.pa_calibrate_mfma.restype = ctypes.c_int
+        L.pa_calibrate_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.pa_calibrate_mfma_flops.restype = ctypes.c_double
         _lib = L
     return _lib
 
@@ -364,3 +369,15 @@ def make_mla_args(*, q, kv_cache, page_table, seq_lens, softmax_scale: float, ou
                        softmax_scale=float(softmax_scale), softcap=float(softcap), out=_ptr(out),
                        o_stride_t=o_stride_t, lse=_ptr(lse), workspace=_ptr(workspace),
                        workspace_bytes=ws_bytes)
+
+
+def pa_calibrate_mfma(operands, sink, num_workgroups: int, iters: int, stream) -> None:
+    """MFMA-rate measurement launch (operands: num_workgroups * 32768 bf16,
+    sink: num_workgroups * 256 float32, both device tensors)."""
+    rc = lib().pa_calibrate_mfma(_ptr(operands), _ptr(sink), int(num_workgroups), int(iters), stream)
+    if rc != PA_OK:
+        raise PaError(rc, "pa_calibrate_mfma")
+
+
+def pa_calibrate_mfma_flops(num_workgroups: int, iters: int) -> float:
+    return float(lib().pa_calibrate_mfma_flops(int(num_workgroups), int(iters)))

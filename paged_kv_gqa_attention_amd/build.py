@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-SOURCES = ["pa_kernels.hip", "pa_api.cpp"]
+SOURCES = ["pa_kernels.hip", "pa_calib.hip", "pa_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

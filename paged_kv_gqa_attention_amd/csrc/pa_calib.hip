@@ -1,0 +1,74 @@
+// pa_calib.hip -- measurement kernel: the dense bf16 MFMA rate one MI355X
+// sustains on random operands.
+//
+// The published dense bf16 peak (256 CUs x 4 SIMDs x 2.4 GHz x 1024 flop per
+// SIMD clock) assumes every SIMD retires one v_mfma_f32_32x32x16_bf16 every
+// 32 clocks at the full clock.  Under a long matrix-core load the chip lowers
+// its clock, and how far depends on how much the operand bits toggle.  This
+// kernel does nothing but MFMAs on caller-supplied (random) operands, so its
+// rate is the practical ceiling against which an attention kernel's MFMA use
+// can be read.  It is not part of the attention path.
+#include "pa_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8c __attribute__((ext_vector_type(8)));
+typedef float f32x16c __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4c __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesPerGroup = 4;
+constexpr int kOps = 8;          // distinct A and B operands per lane
+constexpr int kChains = 4;       // independent accumulators per wave
+
+// Each wave: 8 A and 8 B operands (16 bytes per lane each) from `ops`, four
+// accumulator chains; one loop iteration issues 64 MFMAs, pairing A operand j
+// with B operand (j + r) mod 8 in round r, so consecutive MFMAs never see the
+// same pair of inputs.  The accumulators are summed into `sink` so that no
+// MFMA is dead.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(const uint16_t* __restrict__ ops,
+                                                        float* __restrict__ sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const u32x4c* src = reinterpret_cast<const u32x4c*>(ops) + (int64_t)gw * 2 * kOps * 64 + lane;
+  bf16x8c a[kOps], b[kOps];
+#pragma unroll
+  for (int j = 0; j < kOps; ++j) {
+    a[j] = __builtin_bit_cast(bf16x8c, src[64 * j]);
+    b[j] = __builtin_bit_cast(bf16x8c, src[64 * (kOps + j)]);
+  }
+  f32x16c acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < kOps; ++r)
+#pragma unroll
+      for (int j = 0; j < kOps; ++j)
+        acc[j % kChains] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], b[(j + r) % kOps], acc[j % kChains], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  sink[(int64_t)gw * 64 + lane] = s;
+}
+
+}  // namespace
+
+extern "C" pa_status pa_calibrate_mfma(const uint16_t* operands, float* sink, int32_t num_workgroups,
+                                       int32_t iters, hipStream_t stream) {
+  if (!operands || !sink || num_workgroups <= 0 || iters <= 0) return PA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(operands) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
+    return PA_ERR_INVALID;
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3(num_workgroups), dim3(64 * kWavesPerGroup), 0, stream, operands, sink,
+                     iters);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+extern "C" double pa_calibrate_mfma_flops(int32_t num_workgroups, int32_t iters) {
+  return (double)num_workgroups * kWavesPerGroup * iters * kOps * kOps * (2.0 * 32 * 32 * 16);
+}

@@ -1224,6 +1224,11 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
   fetch(0);
   fetch(1);
   __builtin_amdgcn_sched_barrier(0);
+  // Wave priorities: the score phase (MFMAs interleaved with this step's
+  // exps) goes first, the PV burst second, the row max, mask and loop work
+  // last, so that of the waves sharing a SIMD the one that can feed the
+  // matrix core and the VALU at once is issued first.
+  __builtin_amdgcn_s_setprio(3);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     fetch(j + 2);
@@ -1236,6 +1241,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   bf16x8 pb[2];
   pb[0] = pack_bf16x8(p);
   pb[1] = pack_bf16x8(p + 8);
@@ -1243,6 +1249,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = p[i] + p[i + 8];
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     fetch(NQ + v + 2);
@@ -1253,6 +1260,7 @@ __device__ __forceinline__ void stream_step(SoftmaxState<D>& st, const f32x16& s
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   st.l += (q[0] + q[2]) + (q[1] + q[3]);
 }
 

@@ -323,3 +323,13 @@ def test_check_metadata_rejects_bad_arguments_without_touching_the_device():
     assert B.lib().pa_check_metadata(None, ctypes.byref(a), ctypes.c_void_p(4096), None) == B.PA_ERR_INVALID
     assert B.lib().pa_check_metadata(p, None, ctypes.c_void_p(4096), None) == B.PA_ERR_INVALID
     B.pa_plan_destroy(p)
+
+
+def test_calibrate_mfma_rejects_bad_arguments_on_the_host():
+    lib = B.lib()
+    assert lib.pa_calibrate_mfma(None, None, 1, 1, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, 16, 0, 1, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, 16, 1, 0, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(8, 16, 1, 1, None) == B.PA_ERR_INVALID      # operands not 16-byte aligned
+    # 4 waves x 64 MFMAs per trip x 2*32*32*16 flop
+    assert lib.pa_calibrate_mfma_flops(3, 5) == 3 * 4 * 5 * 64 * 32768
