@@ -220,8 +220,10 @@ typedef struct {
 
 /* Validate a shape description and build a plan.  Host only; uses the HIP
  * runtime only when desc->num_cus == 0.  Returns PA_ERR_INVALID for malformed
- * descriptions and PA_ERR_UNSUPPORTED for geometry outside the compiled scope;
- * *out is set only on PA_OK.  One plan per batch shape, metadata bound at run
+ * descriptions and PA_ERR_UNSUPPORTED for geometry outside the compiled scope
+ * (this includes a page of 2^32 bytes or more, kv_page_stride included, and a
+ * slot of 2^24 bytes or more, num_kv_heads * head_dim * element size: the
+ * kernels address pages with 32-bit products); *out is set only on PA_OK.  One plan per batch shape, metadata bound at run
  * time, unsupported requests refused so the caller can fall back: TensorRT-LLM
  * PR #17399, "Planning, preprocessing, and workspace ownership" and
  * "Integration and supported scope". */

@@ -89,6 +89,10 @@ pa_status pa_plan(const pa_desc* desc, pa_plan_t* out) {
   const int64_t dense_page = (int64_t)d.page_size * d.num_kv_heads * d.head_dim;
   const int64_t page_elems = d.kv_page_stride ? d.kv_page_stride : dense_page;
   if (page_elems < dense_page || (page_elems * esz) % 16 != 0) return PA_ERR_INVALID;
+  // the kernels form a page base as a 32 x 32 -> 64-bit product and the
+  // offset of a slot inside its page with a 24-bit multiply
+  if (page_elems * esz >= (int64_t(1) << 32)) return PA_ERR_UNSUPPORTED;
+  if ((int64_t)d.num_kv_heads * d.head_dim * esz >= (int64_t(1) << 24)) return PA_ERR_UNSUPPORTED;
   const int64_t capacity = (int64_t)d.page_table_cols * d.page_size;
   if (capacity > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   if (d.max_seq_len > capacity) return PA_ERR_INVALID;
@@ -480,6 +484,7 @@ pa_status pa_mla_plan(const pa_mla_desc* desc, pa_mla_plan_t* out) {
   const int64_t dense_page = (int64_t)d.page_size * kMlaDk;
   const int64_t page_elems = d.kv_page_stride ? d.kv_page_stride : dense_page;
   if (page_elems < dense_page || (page_elems * 2) % 16 != 0) return PA_ERR_INVALID;
+  if (page_elems * 2 >= (int64_t(1) << 32)) return PA_ERR_UNSUPPORTED;   // 32-bit page bytes
   const int64_t capacity = (int64_t)d.page_table_cols * d.page_size;
   if (capacity > INT32_MAX / 2) return PA_ERR_UNSUPPORTED;
   if (d.max_seq_len > capacity) return PA_ERR_INVALID;

@@ -1133,21 +1133,25 @@ struct TileLoads {
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
                                         const PageWalk& w, int key0, uint8_t* buf, int wave) const {
     const int slot_mask = (1 << w.shift) - 1;
-    // page ids of all loads first (one LDS round trip), then the loads
-    int key[per_wave], page[per_wave];
+    // page ids of all loads first (one LDS round trip), then the loads; a
+    // page base is one 32 x 32 -> 64-bit multiply-add and a slot offset one
+    // 24-bit multiply-add (page bytes < 2^32, slot stride < 2^24: the plan
+    // refuses larger geometry)
+    int key[per_wave];
+    uint32_t page[per_wave];
 #pragma unroll
     for (int j = 0; j < per_wave; ++j) {
       key[j] = min(key0 + (int)(slot_rc[j] >> 16), w.kend - 1);
-      page[j] = w.pcache[(key[j] >> w.shift) - w.first_page];
+      page[j] = (uint32_t)w.pcache[(key[j] >> w.shift) - w.first_page];
     }
 #pragma unroll
     for (int j = 0; j < per_wave; ++j) {
       const int i = wave + j * NW;
       if (i < Gm::ring_loads) {
-        const uint8_t* pool = i < Gm::k_slots ? kpool : vpool;
-        const uint8_t* src = pool + (int64_t)page[j] * w.page_bytes + w.head_off +
-                             ((uint32_t)(key[j] & slot_mask) * (uint32_t)w.row_stride_b + (slot_rc[j] & 0xFFFFu));
-        dma_load_16(src, buf + 1024 * i);
+        const uint8_t* pool = (i < Gm::k_slots ? kpool : vpool) + w.head_off;
+        const uint32_t in_page = __umul24((uint32_t)(key[j] & slot_mask), (uint32_t)w.row_stride_b) +
+                                 (slot_rc[j] & 0xFFFFu);
+        dma_load_16(pool + ((uint64_t)page[j] * (uint32_t)w.page_bytes + in_page), buf + 1024 * i);
       }
     }
   }
@@ -1342,6 +1346,8 @@ __device__ __forceinline__ void stream_step_f8(SoftmaxState<D>& st, const f32x16
   for (int i = 0; i < 16; ++i) sn[i] = 0.f;
   i32x8 ka = k_operand_f8<KPITCH>(kl, 0, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
+  // wave priorities by phase, as in stream_step
+  __builtin_amdgcn_s_setprio(3);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     sn = mfma32_f8(ka, q8_operand(qrow, j), sn);
@@ -1353,6 +1359,7 @@ __device__ __forceinline__ void stream_step_f8(SoftmaxState<D>& st, const f32x16
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(1);
   float q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = p[i] + p[i + 8];
@@ -1377,6 +1384,7 @@ __device__ __forceinline__ void stream_step_f8(SoftmaxState<D>& st, const f32x16
       st.o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, st.o[t], 0, 0, 0, 127, 0, e);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Tiles are issued NB-2 ahead: at the top of tile t every wave has waited for

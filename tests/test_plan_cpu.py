@@ -90,6 +90,9 @@ def test_static_decode_host_checks():
     (dict(kv_dtype=7), B.PA_ERR_INVALID),
     (dict(max_seq_len=10_000), B.PA_ERR_INVALID),                    # > C * page
     (dict(kv_page_stride=100), B.PA_ERR_INVALID),                     # < dense page
+    (dict(kv_page_stride=1 << 31), B.PA_ERR_UNSUPPORTED),             # page bytes >= 2^32
+    (dict(kv_page_stride=(1 << 31) - 8), B.PA_OK),                    # page bytes < 2^32
+    (dict(num_q_heads=32768, num_kv_heads=32768, head_dim=256), B.PA_ERR_UNSUPPORTED),  # slot stride 2^24 bytes
     (dict(num_splits=-2), B.PA_ERR_INVALID),
     (dict(num_q_heads=64, num_kv_heads=2, head_dim=256, page_size=128, kv_dtype=B.PA_KV_FP8_E4M3), B.PA_OK),
     (dict(num_q_heads=4, num_kv_heads=4, head_dim=64), B.PA_OK),       # MHA
