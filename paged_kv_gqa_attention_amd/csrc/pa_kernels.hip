@@ -1136,7 +1136,9 @@ struct TileLoads {
     // page ids of all loads first (one LDS round trip), then the loads; a
     // page base is one 32 x 32 -> 64-bit multiply-add and a slot offset one
     // 24-bit multiply-add (page bytes < 2^32, slot stride < 2^24: the plan
-    // refuses larger geometry)
+    // refuses larger geometry).  The fp8 instance keeps the 64-bit product:
+    // there the shorter form gains nothing and its registers tip the kernel
+    // into scratch.
     int key[per_wave];
     uint32_t page[per_wave];
 #pragma unroll
@@ -1149,9 +1151,15 @@ struct TileLoads {
       const int i = wave + j * NW;
       if (i < Gm::ring_loads) {
         const uint8_t* pool = (i < Gm::k_slots ? kpool : vpool) + w.head_off;
-        const uint32_t in_page = __umul24((uint32_t)(key[j] & slot_mask), (uint32_t)w.row_stride_b) +
-                                 (slot_rc[j] & 0xFFFFu);
-        dma_load_16(pool + ((uint64_t)page[j] * (uint32_t)w.page_bytes + in_page), buf + 1024 * i);
+        if constexpr (FP8) {
+          dma_load_16(pool + (int64_t)(int32_t)page[j] * w.page_bytes +
+                          ((uint32_t)(key[j] & slot_mask) * (uint32_t)w.row_stride_b + (slot_rc[j] & 0xFFFFu)),
+                      buf + 1024 * i);
+        } else {
+          const uint32_t in_page = __umul24((uint32_t)(key[j] & slot_mask), (uint32_t)w.row_stride_b) +
+                                   (slot_rc[j] & 0xFFFFu);
+          dma_load_16(pool + ((uint64_t)page[j] * (uint32_t)w.page_bytes + in_page), buf + 1024 * i);
+        }
       }
     }
   }

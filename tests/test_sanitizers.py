@@ -42,8 +42,9 @@ def run(cmd, **kw):
 def test_cpu_suite_under_asan_and_ubsan(tmp_path):
     if os.environ.get("PA_SANITIZED_CHILD"):
         pytest.skip("already inside the sanitized run")
-    kobj = os.path.join(PKG, "_build", "pa_kernels.hip.o")
-    if not os.path.exists(kobj):
+    # the device-code objects of libpa.so as build.py compiled them
+    kobjs = [os.path.join(PKG, "_build", s + ".o") for s in ("pa_kernels.hip", "pa_calib.hip")]
+    if not all(os.path.exists(k) for k in kobjs):
         pytest.skip("libpa.so has not been built (python -m paged_kv_gqa_attention_amd.build)")
     olib = str(tmp_path / "libpa_oracle_san.so")
     run(["gcc", "-O1", "-std=c99", "-fopenmp", "-shared", "-fPIC"] + SAN +
@@ -53,7 +54,7 @@ def test_cpu_suite_under_asan_and_ubsan(tmp_path):
         ["-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
          "-I", os.path.join(PKG, "csrc"), "-c", os.path.join(PKG, "csrc", "pa_api.cpp"), "-o", aobj])
     lib = str(tmp_path / "libpa_san.so")
-    run(["g++", "-shared"] + SAN + ["-o", lib, aobj, kobj, "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+    run(["g++", "-shared"] + SAN + ["-o", lib, aobj] + kobjs + ["-L", os.path.join(ROCM, "lib"), "-lamdhip64",
                                     "-Wl,-rpath," + os.path.join(ROCM, "lib")])
     asan = run(["gcc", "-print-file-name=libasan.so"]).stdout.strip()
     env = dict(os.environ)
