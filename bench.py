@@ -327,40 +327,52 @@ def cpu_model() -> str:
 
 
 def mfma_ceiling(iters: int = 1000, launches: int = 10):
-    """Sustained dense bf16 MFMA rate of this GPU (pa_calibrate_mfma): three
-    waves per SIMD doing nothing but v_mfma_f32_32x32x16_bf16, on random
-    N(0,1) bf16 operands and, for comparison, on zeros (the chip's clock under
-    a matrix-core load depends on how much the operand bits toggle).  The
-    random-operand rate is the practical ceiling of the MFMA-bound lines; their
-    roofline fractions stay taken against the published peak."""
+    """Sustained dense MFMA rate of this GPU (pa_calibrate_mfma): two waves per
+    SIMD doing nothing but v_mfma_f32_32x32x16_bf16, or E4M3
+    v_mfma_scale_f32_32x32x64_f8f6f4, on random N(0,1) operands
+    and, for comparison, on zeros (the chip's clock under a matrix-core load
+    depends on how much the operand bits toggle).  The random-operand rates
+    are the practical ceilings of the MFMA-bound lines; their roofline
+    fractions stay taken against the published peaks."""
     import torch
     from paged_kv_gqa_attention_amd import binding
-    # 136 VGPRs per wave: three 4-wave workgroups per CU, all resident at once
-    nwg = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     gen = torch.Generator(device="cuda").manual_seed(7)
+    stream = binding.current_stream()
     res = {}
-    for kind in ("random", "zeros"):
-        ops = torch.randn(nwg * 32768, generator=gen, device="cuda").to(torch.bfloat16)
-        if kind == "zeros":
-            ops.zero_()
-        sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
-        stream = binding.current_stream()
-        for _ in range(2):
-            binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream)
-        torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(launches):
-            binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream)
-        e.record()
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / launches
-        res[kind] = binding.pa_calibrate_mfma_flops(nwg, iters) / (ms * 1e-3) / 1e12
-    return {"tflops": round(res["random"], 1), "frac_of_peak": round(res["random"] / BF16_PEAK_TFLOPS, 4),
-            "zero_operand_tflops": round(res["zeros"], 1),
-            "kernel": "pa_calibrate_mfma: v_mfma_f32_32x32x16_bf16 only, 3 waves per SIMD",
-            "operands": "random N(0,1) bf16 (zero_operand_tflops: all zeros)"}
+    for fp8 in (False, True):
+        # about 200 VGPRs per wave: two four-wave workgroups per compute unit,
+        # every workgroup resident at once
+        nwg = 2 * cus
+        words = nwg * (65536 if fp8 else 32768)
+        for kind in ("random", "zeros"):
+            # E4M3: two codes per 16-bit word, every code a finite value
+            x = torch.randn(words * (2 if fp8 else 1), generator=gen, device="cuda")
+            if kind == "zeros":
+                x.zero_()
+            ops = x.to(torch.float8_e4m3fn).view(torch.int16) if fp8 else x.to(torch.bfloat16)
+            sink = torch.empty(nwg * 256, dtype=torch.float32, device="cuda")
+            for _ in range(2):
+                binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream, fp8=fp8)
+            torch.cuda.synchronize()
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(launches):
+                binding.pa_calibrate_mfma(ops, sink, nwg, iters, stream, fp8=fp8)
+            e.record()
+            torch.cuda.synchronize()
+            ms = s.elapsed_time(e) / launches
+            res[(fp8, kind)] = binding.pa_calibrate_mfma_flops(nwg, iters, fp8=fp8) / (ms * 1e-3) / 1e12
+    return {"tflops": round(res[(False, "random")], 1),
+            "frac_of_peak": round(res[(False, "random")] / BF16_PEAK_TFLOPS, 4),
+            "zero_operand_tflops": round(res[(False, "zeros")], 1),
+            "fp8_tflops": round(res[(True, "random")], 1),
+            "fp8_frac_of_peak": round(res[(True, "random")] / FP8_PEAK_TFLOPS, 4),
+            "fp8_zero_operand_tflops": round(res[(True, "zeros")], 1),
+            "kernel": "pa_calibrate_mfma: v_mfma_f32_32x32x16_bf16 only (8 accumulator chains), or "
+                      "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3, no block scales; 4 chains) only, 2 waves per SIMD",
+            "operands": "random N(0,1) bf16 / E4M3 (zero_operand_tflops: all zeros)"}
 
 
 def main():
@@ -500,6 +512,8 @@ def main():
         for e in sec.values():
             if e["roofline"]["unit"] == "TFLOP/s" and e["roofline"]["peak"] == BF16_PEAK_TFLOPS:
                 e["roofline"]["frac_of_mfma_ceiling"] = round(e["roofline"]["achieved"] / ceiling["tflops"], 4)
+            elif e["roofline"]["unit"] == "TFLOP/s" and e["roofline"]["peak"] == FP8_PEAK_TFLOPS:
+                e["roofline"]["frac_of_mfma_ceiling"] = round(e["roofline"]["achieved"] / ceiling["fp8_tflops"], 4)
     w = prim["w"]
     alg_bytes = prim["kv_bytes"] + prim["qo_bytes"]
     achieved = alg_bytes / (prim["ms_per_step"] * 1e-3) / 1e9

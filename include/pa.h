@@ -448,24 +448,30 @@ const char* pa_status_str(pa_status status);
  * Measurement (not part of the attention path)
  *
  * The roofline fractions of the prefill lines are taken against the published
- * dense bf16 MFMA peak; these two calls measure the rate this GPU actually
- * sustains when it does nothing but bf16 MFMAs (v_mfma_f32_32x32x16_bf16) on
- * random operands, the practical ceiling of any MFMA-bound kernel here.  The
- * score and PV products they stand for are the dense contractions of the
- * attention definition (vLLM PR #48156, "Residual warmed gap": kernel time
- * attributed by microbenchmark).
- *   operands  device, 16-byte aligned, num_workgroups * 32768 bf16 values
- *             (4 waves x 16 operands x 64 lanes x 8 values per workgroup),
+ * dense MFMA peaks; these two calls measure the rate this GPU actually
+ * sustains when it does nothing but MFMAs on random operands -- bf16
+ * (v_mfma_f32_32x32x16_bf16) or, with fp8 = 1, OCP E4M3
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 without block scales) -- the practical
+ * ceiling of any MFMA-bound kernel here.  The score and PV products they
+ * stand for are the dense contractions of the attention definition (vLLM PR
+ * #48156, "Residual warmed gap": kernel time attributed by microbenchmark).
+ *   operands  device, 16-byte aligned, num_workgroups * 32768 16-bit words
+ *             (bf16: 4 waves x 16 operands x 64 lanes x 16 bytes per
+ *             workgroup) or num_workgroups * 65536 (fp8: 32-byte operands),
  *             read once; the caller fills them (random values for the ceiling)
  *   sink      device, num_workgroups * 256 floats, written (the accumulators'
  *             sums, so that no product is dead code)
  *   iters     loop trips; each wave issues 64 MFMAs per trip
- * Errors: PA_ERR_INVALID for null or misaligned pointers or non-positive
- * sizes, PA_ERR_HIP when the launch fails.  pa_calibrate_mfma_flops returns
- * the floating-point operations one such launch performs. */
+ *   fp8       0: bf16 operands, 1: E4M3 operands
+ * A wave holds about 200 registers: two four-wave workgroups per compute
+ * unit are resident at once.
+ * Errors: PA_ERR_INVALID for null or misaligned pointers, non-positive sizes
+ * or fp8 outside {0, 1}, PA_ERR_HIP when the launch fails.
+ * pa_calibrate_mfma_flops returns the floating-point operations one such
+ * launch performs. */
 pa_status pa_calibrate_mfma(const uint16_t* operands, float* sink, int32_t num_workgroups, int32_t iters,
-                            hipStream_t stream);
-double pa_calibrate_mfma_flops(int32_t num_workgroups, int32_t iters);
+                            int32_t fp8, hipStream_t stream);
+double pa_calibrate_mfma_flops(int32_t num_workgroups, int32_t iters, int32_t fp8);
 
 #ifdef __cplusplus
 }

@@ -207,9 +207,9 @@ def lib():
         L.pa_run_mla_decode.restype = ctypes.c_int
         L.pa_mla_plan_destroy.argtypes = [vp]
         L.pa_mla_plan_destroy.restype = None
-        L.pa_calibrate_mfma.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
+        L.pa_calibrate_mfma.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
         L.pa_calibrate_mfma.restype = ctypes.c_int
-        L.pa_calibrate_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.pa_calibrate_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.pa_calibrate_mfma_flops.restype = ctypes.c_double
         _lib = L
     return _lib
@@ -371,13 +371,15 @@ def make_mla_args(*, q, kv_cache, page_table, seq_lens, softmax_scale: float, ou
                        workspace_bytes=ws_bytes)
 
 
-def pa_calibrate_mfma(operands, sink, num_workgroups: int, iters: int, stream) -> None:
-    """MFMA-rate measurement launch (operands: num_workgroups * 32768 bf16,
-    sink: num_workgroups * 256 float32, both device tensors)."""
-    rc = lib().pa_calibrate_mfma(_ptr(operands), _ptr(sink), int(num_workgroups), int(iters), stream)
+def pa_calibrate_mfma(operands, sink, num_workgroups: int, iters: int, stream, fp8: bool = False) -> None:
+    """MFMA-rate measurement launch (operands: num_workgroups * 32768 16-bit
+    words for bf16, 65536 for E4M3; sink: num_workgroups * 256 float32; both
+    device tensors)."""
+    rc = lib().pa_calibrate_mfma(_ptr(operands), _ptr(sink), int(num_workgroups), int(iters), int(bool(fp8)),
+                                 stream)
     if rc != PA_OK:
         raise PaError(rc, "pa_calibrate_mfma")
 
 
-def pa_calibrate_mfma_flops(num_workgroups: int, iters: int) -> float:
-    return float(lib().pa_calibrate_mfma_flops(int(num_workgroups), int(iters)))
+def pa_calibrate_mfma_flops(num_workgroups: int, iters: int, fp8: bool = False) -> float:
+    return float(lib().pa_calibrate_mfma_flops(int(num_workgroups), int(iters), int(bool(fp8))))
