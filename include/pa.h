@@ -465,12 +465,15 @@ const char* pa_status_str(pa_status status);
  *   fp8       0: bf16 operands, 1: E4M3 operands
  * A wave holds about 200 registers: two four-wave workgroups per compute
  * unit are resident at once.
- * Errors: PA_ERR_INVALID for null or misaligned pointers, non-positive sizes
- * or fp8 outside {0, 1}, PA_ERR_HIP when the launch fails.
+ *   operand_words, sink_floats  the sizes of those two buffers, checked
+ *             against what the launch reads and writes
+ * Errors: PA_ERR_INVALID for null or misaligned pointers, non-positive sizes,
+ * buffers smaller than the launch needs or fp8 outside {0, 1}, PA_ERR_HIP
+ * when the launch fails.
  * pa_calibrate_mfma_flops returns the floating-point operations one such
  * launch performs. */
-pa_status pa_calibrate_mfma(const uint16_t* operands, float* sink, int32_t num_workgroups, int32_t iters,
-                            int32_t fp8, hipStream_t stream);
+pa_status pa_calibrate_mfma(const uint16_t* operands, int64_t operand_words, float* sink, int64_t sink_floats,
+                            int32_t num_workgroups, int32_t iters, int32_t fp8, hipStream_t stream);
 double pa_calibrate_mfma_flops(int32_t num_workgroups, int32_t iters, int32_t fp8);
 
 #ifdef __cplusplus

@@ -207,7 +207,8 @@ def lib():
         L.pa_run_mla_decode.restype = ctypes.c_int
         L.pa_mla_plan_destroy.argtypes = [vp]
         L.pa_mla_plan_destroy.restype = None
-        L.pa_calibrate_mfma.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
+        L.pa_calibrate_mfma.argtypes = [vp, ctypes.c_int64, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, vp]
         L.pa_calibrate_mfma.restype = ctypes.c_int
         L.pa_calibrate_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
         L.pa_calibrate_mfma_flops.restype = ctypes.c_double
@@ -375,8 +376,8 @@ def pa_calibrate_mfma(operands, sink, num_workgroups: int, iters: int, stream, f
     """MFMA-rate measurement launch (operands: num_workgroups * 32768 16-bit
     words for bf16, 65536 for E4M3; sink: num_workgroups * 256 float32; both
     device tensors)."""
-    rc = lib().pa_calibrate_mfma(_ptr(operands), _ptr(sink), int(num_workgroups), int(iters), int(bool(fp8)),
-                                 stream)
+    rc = lib().pa_calibrate_mfma(_ptr(operands), int(operands.numel() * operands.element_size() // 2), _ptr(sink),
+                                 int(sink.numel()), int(num_workgroups), int(iters), int(bool(fp8)), stream)
     if rc != PA_OK:
         raise PaError(rc, "pa_calibrate_mfma")
 

@@ -84,9 +84,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
 
 }  // namespace
 
-extern "C" pa_status pa_calibrate_mfma(const uint16_t* operands, float* sink, int32_t num_workgroups,
-                                       int32_t iters, int32_t fp8, hipStream_t stream) {
+extern "C" pa_status pa_calibrate_mfma(const uint16_t* operands, int64_t operand_words, float* sink,
+                                       int64_t sink_floats, int32_t num_workgroups, int32_t iters, int32_t fp8,
+                                       hipStream_t stream) {
   if (!operands || !sink || num_workgroups <= 0 || iters <= 0 || (fp8 != 0 && fp8 != 1)) return PA_ERR_INVALID;
+  // every wave reads 2 * 8 operands of 64 lanes x 16 (bf16) or 32 (E4M3) bytes
+  // and writes 64 floats
+  if (operand_words < (int64_t)num_workgroups * (fp8 ? 65536 : 32768) ||
+      sink_floats < (int64_t)num_workgroups * 64 * kWavesPerGroup)
+    return PA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(operands) & 15) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3) != 0)
     return PA_ERR_INVALID;
   if (fp8)

@@ -330,11 +330,16 @@ def test_check_metadata_rejects_bad_arguments_without_touching_the_device():
 
 def test_calibrate_mfma_rejects_bad_arguments_on_the_host():
     lib = B.lib()
-    assert lib.pa_calibrate_mfma(None, None, 1, 1, 0, None) == B.PA_ERR_INVALID
-    assert lib.pa_calibrate_mfma(16, 16, 0, 1, 0, None) == B.PA_ERR_INVALID
-    assert lib.pa_calibrate_mfma(16, 16, 1, 0, 0, None) == B.PA_ERR_INVALID
-    assert lib.pa_calibrate_mfma(8, 16, 1, 1, 0, None) == B.PA_ERR_INVALID      # operands not 16-byte aligned
-    assert lib.pa_calibrate_mfma(16, 16, 1, 1, 2, None) == B.PA_ERR_INVALID     # fp8 flag outside {0, 1}
+    big = 1 << 40
+    assert lib.pa_calibrate_mfma(None, big, None, big, 1, 1, 0, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, big, 16, big, 0, 1, 0, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, big, 16, big, 1, 0, 0, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(8, big, 16, big, 1, 1, 0, None) == B.PA_ERR_INVALID     # operands not 16-byte aligned
+    assert lib.pa_calibrate_mfma(16, big, 16, big, 1, 1, 2, None) == B.PA_ERR_INVALID    # fp8 flag outside {0, 1}
+    # buffers one element short of what two workgroups read and write
+    assert lib.pa_calibrate_mfma(16, 2 * 32768 - 1, 16, big, 2, 1, 0, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, 2 * 65536 - 1, 16, big, 2, 1, 1, None) == B.PA_ERR_INVALID
+    assert lib.pa_calibrate_mfma(16, big, 16, 2 * 256 - 1, 2, 1, 0, None) == B.PA_ERR_INVALID
     # 4 waves x 64 MFMAs per trip x 2*32*32*K flop (K = 16 bf16, 64 E4M3)
     assert lib.pa_calibrate_mfma_flops(3, 5, 0) == 3 * 4 * 5 * 64 * 32768
     assert lib.pa_calibrate_mfma_flops(3, 5, 1) == 3 * 4 * 5 * 64 * 131072
